@@ -24,10 +24,15 @@ summation, far below any tolerance used.
 Two non-negative bound matrices come with it:
 
 * S[m, n] = sum_k |a_k b_k|  (the sum of product magnitudes, dequantised);
-* G[m, n] = sum_g (max_{k in g} |a_k|)(max_{k in g} |b_k|) over the aligned
-  groups g of 8 consecutive k -- an upper bound of sum_g max_{k in g} |a_k b_k|,
-  used by the tests to bound the error of an accumulator that sums short runs
-  of products at reduced precision before promoting them to fp32.
+* G[m, n] = sum_g alpha_g beta_g (max_{k in g} 2^ea_k)(max_{k in g} 2^eb_k) over
+  the aligned groups g of 8 consecutive k, where ea / eb is the binade exponent
+  of the FP8 code (exponent field minus bias; the minimum normal exponent for
+  subnormals and zeros) and alpha_g / beta_g the group's dequantisation factors.
+  Since |a| < 2^(ea+1) for every code, 4 G bounds sum_g max_{k in g} |a_k b_k|.
+  The tests use G to bound the error of an accumulator that sums each run of 8
+  products in a fixed-point window below its largest exponent sum before
+  promoting the run to fp32 (the course page's "about 14 bits", measured on the
+  matrix cores this path runs on).
 
 A bf16 output is the float32 result rounded to nearest even (``oracle.fp8``).
 """
@@ -66,24 +71,37 @@ def dequant(q, fmt, gran, scale_inv) -> np.ndarray:
     raise ValueError("granularity")
 
 
-def group_max(v, group: int = 8) -> np.ndarray:
-    """max |v| over aligned runs of ``group`` columns -> [rows][K/group]."""
-    a = np.abs(v)
-    rows, k = a.shape
-    return a.reshape(rows, k // group, group).max(axis=2)
+def code_binade(q, fmt) -> np.ndarray:
+    """2^e for each FP8 code: e = exponent field - bias (1 - bias for subnormals and zero)."""
+    mbits, bias = (3, 7) if fmt == fp8.E4M3 else (2, 15)
+    ef = (np.asarray(q, dtype=np.uint8).astype(np.int64) & 0x7F) >> mbits
+    return np.exp2((np.maximum(ef, 1) - bias).astype(np.float64))
+
+
+def group_exponent_bound(q, fmt, gran, scale_inv, group: int = 8) -> np.ndarray:
+    """[rows][K/group]: max over each run of 2^e(code), times the run's dequantisation factor."""
+    rows, k = np.asarray(q).shape
+    e = code_binade(q, fmt).reshape(rows, k // group, group).max(axis=2)
+    ones = np.ones((rows, k), dtype=np.uint8) * 0x38  # 1.0 in E4M3: picks out the factors
+    f = dequant(ones, fp8.E4M3, gran, scale_inv)[:, ::group]
+    return e * f
 
 
 def gemm_ref(A, fmt_a, sa, gran_a, B, fmt_b, sb, gran_b, rows=None, cols=None):
     """(C, S, G) in float64 for C = A . B^T; optional row / column subsets of the output."""
+    A = np.asarray(A, dtype=np.uint8)
+    B = np.asarray(B, dtype=np.uint8)
     Ad = dequant(A, fmt_a, gran_a, sa)
     Bd = dequant(B, fmt_b, gran_b, sb)
+    Ae = group_exponent_bound(A, fmt_a, gran_a, sa)
+    Be = group_exponent_bound(B, fmt_b, gran_b, sb)
     if rows is not None:
-        Ad = Ad[rows]
+        Ad, Ae = Ad[rows], Ae[rows]
     if cols is not None:
-        Bd = Bd[cols]
+        Bd, Be = Bd[cols], Be[cols]
     C = Ad @ Bd.T
     S = np.abs(Ad) @ np.abs(Bd).T
-    G = group_max(Ad) @ group_max(Bd).T
+    G = Ae @ Be.T
     return C, S, G
 
 

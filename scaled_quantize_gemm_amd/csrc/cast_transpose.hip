@@ -1,0 +1,169 @@
+// Per-tensor FP8 cast and its transpose in one pass (+ amax).
+//
+// The hybrid recipe's backward pass ("Transformer Scaling" lesson, Part 01: E4M3 forward,
+// wider-range E5M2 gradients; "Week 14" course page, FP8 bullet) multiplies by transposed
+// operands.  Writing the transposed FP8 copy during the cast keeps every GEMM in the
+// K-contiguous form without a second read of the high-precision tensor.
+//
+// Tile 64 x 64, 256 threads, persistent grid-stride over tiles:
+//   phase 1: thread (row r, 8-column chunk) loads 8 elements of rows r and r+32, casts them,
+//            stores the 8 codes to q and to an LDS tile (dword pitch 17 to spread banks);
+//   phase 2: thread (4-column group, 4-row group) reads 4 dwords (4 rows x 4 columns),
+//            transposes the 4x4 bytes in registers with v_perm_b32 and stores one dword
+//            (4 consecutive source rows) to each of 4 rows of qT; 16 lanes cover 64
+//            contiguous bytes of a qT row.
+// Tiles that are partial or whose rows are not 16-byte aligned take an element-wise path.
+#include "common.h"
+
+namespace sfp8 {
+
+constexpr int kCtTile = 64;
+constexpr int kCtPitch = 17;  // dwords per LDS row (16 + 1 pad)
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t elem, float (&v)[8]) {
+  if constexpr (BF16) {
+    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem));
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + elem);
+    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld1(const void* __restrict__ base, int64_t i) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+  else return static_cast<const float*>(base)[i];
+}
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256) cast_transpose_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                             const float* __restrict__ scale_p,
+                                                             uint32_t* __restrict__ amax_slot, uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ qT) {
+  __shared__ uint32_t lds[kCtTile * kCtPitch];
+  __shared__ uint32_t red[4];
+  const float s = *scale_p;
+  const int t = threadIdx.x;
+  const int64_t tiles_c = (cols + kCtTile - 1) / kCtTile;
+  const int64_t ntiles = ((rows + kCtTile - 1) / kCtTile) * tiles_c;
+  const bool aligned_rows = (cols % 8 == 0) && (rows % 4 == 0);
+  uint32_t mx = 0;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t r0 = (tile / tiles_c) * kCtTile, c0 = (tile % tiles_c) * kCtTile;
+    const bool full = aligned_rows && r0 + kCtTile <= rows && c0 + kCtTile <= cols;
+    if (full) {
+      const int cg = t & 7, rr = t >> 3;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = rr + 32 * h;
+        const int64_t e0 = (r0 + r) * cols + c0 + cg * 8;
+        float v[8];
+        load8<BF16>(x, e0, v);
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t a = abs_bits(v[i]);
+          m = m > a ? m : a;
+        }
+        uint32_t w0 = cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+        uint32_t w1 = cvt4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+        if (m > 0x7F800000u) {
+          w0 = patch_nan4(w0, &v[0]);
+          w1 = patch_nan4(w1, &v[4]);
+        }
+        mx = mx > m ? mx : m;
+        *reinterpret_cast<uint2*>(q + e0) = make_uint2(w0, w1);
+        lds[r * kCtPitch + cg * 2] = w0;
+        lds[r * kCtPitch + cg * 2 + 1] = w1;
+      }
+      __syncthreads();
+      const int g4 = t >> 4, rc = t & 15;  // 4-column group, 4-row group
+      uint32_t d0 = lds[(4 * rc + 0) * kCtPitch + g4];
+      uint32_t d1 = lds[(4 * rc + 1) * kCtPitch + g4];
+      uint32_t d2 = lds[(4 * rc + 2) * kCtPitch + g4];
+      uint32_t d3 = lds[(4 * rc + 3) * kCtPitch + g4];
+      // 4x4 byte transpose: out_j byte i = d_i byte j
+      uint32_t lo01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+      uint32_t hi01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+      uint32_t lo23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+      uint32_t hi23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+      uint32_t o[4];
+      o[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+      o[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+      o[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+      o[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(qT + (c0 + 4 * g4 + j) * rows + r0 + 4 * rc) = o[j];
+      __syncthreads();  // the LDS tile is rewritten by the next tile
+    } else {
+      for (int e = t; e < kCtTile * kCtTile; e += 256) {
+        const int64_t r = r0 + (e >> 6), c = c0 + (e & 63);
+        if (r < rows && c < cols) {
+          float xv = ld1<BF16>(x, r * cols + c);
+          uint32_t w = cvt_pair<FMT, false>(xv * s, 0.0f, 0u) & 0xFFu;
+          uint32_t b = __float_as_uint(xv);
+          uint32_t a = b & 0x7FFFFFFFu;
+          if (a > 0x7F800000u) w = nan_code(b);
+          mx = mx > a ? mx : a;
+          q[r * cols + c] = (uint8_t)w;
+          qT[c * rows + r] = (uint8_t)w;
+        }
+      }
+    }
+  }
+  uint32_t r = wave_max_u32(mx);
+  if ((t & 63) == 0) red[t >> 6] = r;
+  __syncthreads();
+  if (t == 0 && amax_slot != nullptr) {
+    uint32_t b = red[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) b = b > red[i] ? b : red[i];
+    if (b > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_slot, b);
+  }
+}
+
+template <int FMT, bool BF16>
+static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* scale, float* amax_slot, uint8_t* q,
+                     uint8_t* qT, hipStream_t st) {
+  const int64_t ntiles = ((rows + kCtTile - 1) / kCtTile) * ((cols + kCtTile - 1) / kCtTile);
+  const int64_t blocks = ntiles < 4096 ? ntiles : 4096;
+  hipLaunchKernelGGL((cast_transpose_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols,
+                     scale, reinterpret_cast<uint32_t*>(amax_slot), q, qT);
+  return check_launch("fp8_cast_transpose");
+}
+
+}  // namespace sfp8
+
+using namespace sfp8;
+
+extern "C" int fp8_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int fmt, const float* scale,
+                                  float* amax_slot, uint8_t* q, uint8_t* qT, void* stream) {
+  SFP8_REQUIRE(rows >= 0 && cols >= 0, FP8_ERR_SHAPE, "fp8_cast_transpose: negative shape (%lld, %lld)",
+               (long long)rows, (long long)cols);
+  SFP8_REQUIRE(x_dtype == HP_F32 || x_dtype == HP_BF16, FP8_ERR_DTYPE, "fp8_cast_transpose: x_dtype %d", x_dtype);
+  SFP8_REQUIRE(fmt == FP8_E4M3 || fmt == FP8_E5M2, FP8_ERR_ARG, "fp8_cast_transpose: fmt %d", fmt);
+  SFP8_REQUIRE(scale != nullptr, FP8_ERR_ARG, "fp8_cast_transpose: null scale");
+  SFP8_REQUIRE(aligned4(scale) && (amax_slot == nullptr || aligned4(amax_slot)), FP8_ERR_ARG,
+               "fp8_cast_transpose: scale / amax_slot must be 4-byte aligned");
+  if (rows * cols == 0) return FP8_OK;
+  SFP8_REQUIRE(x != nullptr && q != nullptr && qT != nullptr, FP8_ERR_ARG, "fp8_cast_transpose: null x, q or qT");
+  SFP8_REQUIRE(aligned16(x) && aligned16(q) && aligned16(qT), FP8_ERR_ARG,
+               "fp8_cast_transpose: x, q and qT must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = x_dtype == HP_BF16;
+  if (fmt == FP8_E4M3)
+    return bf ? launch_ct<FP8_E4M3, true>(x, rows, cols, scale, amax_slot, q, qT, st)
+              : launch_ct<FP8_E4M3, false>(x, rows, cols, scale, amax_slot, q, qT, st);
+  return bf ? launch_ct<FP8_E5M2, true>(x, rows, cols, scale, amax_slot, q, qT, st)
+            : launch_ct<FP8_E5M2, false>(x, rows, cols, scale, amax_slot, q, qT, st);
+}

@@ -1,0 +1,139 @@
+// Shared device helpers and host error plumbing for the FP8 scaled-linear library (gfx950).
+//
+// FP8 encode on gfx950: v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round to nearest even, keep
+// subnormals and the sign of zero -- the encode the pages call for ("Week 14" course page,
+// FP8 bullet and accumulation-precision bullet: ties go to even) -- for every input up to
+// fmax in magnitude.  They do not saturate (E4M3 overflow gives NaN, E5M2 gives inf) and
+// write NaN without its sign, so the cast is: clamp to [-fmax, fmax] with v_med3_f32
+// (which also sends +-inf to +-fmax, the "clips at 448" rule of the "Transformer Scaling"
+// lesson, Worked example 02), convert, and rewrite the byte of any NaN input as
+// sign | 0x7F.  NaN inputs are rare; they are detected from the amax bits the kernels
+// compute anyway, and patched on a per-lane slow path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/scaled_fp8.h"
+
+namespace sfp8 {
+
+// ------------------------------------------------------------------ host-side errors
+
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int check_launch(const char* what);
+
+#define SFP8_REQUIRE(cond, code, ...)        \
+  do {                                       \
+    if (!(cond)) return set_error((code), __VA_ARGS__); \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// ------------------------------------------------------------------ device helpers
+
+// 16-byte vector usable with the nontemporal (streaming) load/store builtins
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 u32x4_make(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return v;
+}
+
+template <int FMT>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<FP8_E4M3> {
+  static constexpr float fmax = 448.0f;
+  // amax <= 1.75 * 2^e  <=>  E = e - 8 (smallest E with amax <= 448 * 2^E)
+  static constexpr int mx_bias = 8;
+};
+template <>
+struct Fp8Traits<FP8_E5M2> {
+  static constexpr float fmax = 57344.0f;
+  static constexpr int mx_bias = 15;
+};
+
+// Two float32 values -> two FP8 codes in bytes (2*hi, 2*hi+1) of `old` (saturating).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b, uint32_t old) {
+  constexpr float fm = Fp8Traits<FMT>::fmax;
+  a = __builtin_amdgcn_fmed3f(a, -fm, fm);
+  b = __builtin_amdgcn_fmed3f(b, -fm, fm);
+  if constexpr (FMT == FP8_E4M3)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
+}
+
+// Four float32 values -> one dword of four FP8 codes (byte i = value i).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  uint32_t w = cvt_pair<FMT, false>(a, b, 0u);
+  return cvt_pair<FMT, true>(c, d, w);
+}
+
+// NaN input bits -> its FP8 code (sign | 0x7F in both formats).
+__device__ __forceinline__ uint32_t nan_code(uint32_t f32bits) { return ((f32bits >> 24) & 0x80u) | 0x7Fu; }
+
+// Replace byte i of `w` by the NaN code of x_i wherever x_i is NaN.
+__device__ __forceinline__ uint32_t patch_nan4(uint32_t w, const float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t b = __float_as_uint(x[i]);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) w = (w & ~(0xFFu << (8 * i))) | (nan_code(b) << (8 * i));
+  }
+  return w;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// |x| bits of a float: unsigned order of these bits is the order of |x|, and every NaN
+// compares above +inf, so an unsigned max propagates NaN.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// Unsigned max over the 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Unsigned max over aligned groups of W lanes (W = 2, 4, 8, 16, 32).
+template <int W>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = W / 2; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Current-scaling rule: s = fmax / amax (correctly rounded), overflow clamped to FLT_MAX;
+// amax zero or not finite -> s = 1.  s_inv = 1 / s.
+template <int FMT>
+__device__ __forceinline__ void current_scale(uint32_t amax_bits, float& s, float& s_inv) {
+  if (amax_bits == 0u || amax_bits >= 0x7F800000u) {
+    s = 1.0f;
+    s_inv = 1.0f;
+    return;
+  }
+  float r = Fp8Traits<FMT>::fmax / __uint_as_float(amax_bits);
+  s = fminf(r, 3.40282346638528859812e+38f);
+  s_inv = 1.0f / s;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+}  // namespace sfp8

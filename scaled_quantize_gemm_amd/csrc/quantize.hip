@@ -1,0 +1,406 @@
+// Fused amax + scale + saturating RNE cast to FP8, at four scale granularities.
+//
+// "Transformer Scaling" lesson, Part 01 (a scale maps values into the FP8 range, often via
+// amax) and Core vocabulary (delayed scaling avoids a second, pre-quantisation read);
+// "Week 14" course page, absmax bullet (per-tensor and per-block scales; MX: a shared
+// scale per 32 numbers; DeepSeek-V3: per 128 activation values and per 128x128 weight block,
+// computed online from the current block).
+//
+// Every kernel reads its input once from HBM and writes the codes once: amax is computed
+// from the same registers the cast reads (delayed scaling records it for the next step;
+// the blockwise and MX kernels hold the whole block in registers, reduce, then cast).
+#include "common.h"
+
+namespace sfp8 {
+
+// ------------------------------------------------------------------ element loaders
+//
+// A chunk is 16 consecutive elements.  bf16: 2 x 16-byte loads; fp32: 4 x 16-byte loads.
+
+template <bool BF16>
+struct Chunk16 {
+  float v[16];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* __restrict__ base, int64_t elem, float (&v)[16], uint32_t& mx) {
+  if constexpr (BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+    u32x4 a = __builtin_nontemporal_load(p);
+    u32x4 b = __builtin_nontemporal_load(p + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+      uint32_t m = w[i] & 0x7FFF7FFFu;
+      uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+      mx = mx > lo ? mx : lo;
+      mx = mx > hi ? mx : hi;
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 a = __builtin_nontemporal_load(p + j);
+      v[4 * j + 0] = __uint_as_float(a.x);
+      v[4 * j + 1] = __uint_as_float(a.y);
+      v[4 * j + 2] = __uint_as_float(a.z);
+      v[4 * j + 3] = __uint_as_float(a.w);
+      uint32_t m0 = a.x & 0x7FFFFFFFu, m1 = a.y & 0x7FFFFFFFu, m2 = a.z & 0x7FFFFFFFu, m3 = a.w & 0x7FFFFFFFu;
+      m0 = m0 > m1 ? m0 : m1;
+      m2 = m2 > m3 ? m2 : m3;
+      m0 = m0 > m2 ? m0 : m2;
+      mx = mx > m0 ? mx : m0;
+    }
+  }
+}
+
+// bits of |x| as float32 bits (bf16 maxima are tracked as 16-bit patterns)
+template <bool BF16>
+__device__ __forceinline__ uint32_t amax_f32_bits(uint32_t mx) {
+  return BF16 ? (mx << 16) : mx;
+}
+template <bool BF16>
+__device__ __forceinline__ bool has_nan(uint32_t mx) {
+  return BF16 ? (mx > 0x7F80u) : (mx > 0x7F800000u);
+}
+
+// 16 values * s -> 4 dwords of codes (NaN inputs patched when `nan` is set).
+template <int FMT>
+__device__ __forceinline__ u32x4 cast16(const float (&v)[16], float s, bool nan) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = cvt4<FMT>(v[4 * j] * s, v[4 * j + 1] * s, v[4 * j + 2] * s, v[4 * j + 3] * s);
+  if (nan) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = patch_nan4(w[j], &v[4 * j]);
+  }
+  return u32x4_make(w[0], w[1], w[2], w[3]);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_one(const void* __restrict__ base, int64_t i) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+  else return static_cast<const float*>(base)[i];
+}
+
+template <int FMT>
+__device__ __forceinline__ uint8_t cast_one(float x, float s) {
+  uint32_t w = cvt_pair<FMT, false>(x * s, 0.0f, 0u) & 0xFFu;
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) w = nan_code(b);
+  return (uint8_t)w;
+}
+
+// Block-wide unsigned max (256 threads) -> returned to every thread.
+__device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) r = r > red[i] ? r : red[i];
+  return r;
+}
+
+// ------------------------------------------------------------------ per-tensor (delayed)
+//
+// Flat stream over n elements.  Each thread handles UNROLL chunks of 16 per iteration of a
+// grid-stride loop; amax is reduced per block and max-ed into *amax_slot with one unsigned
+// atomic per block (|x| bits of non-negative floats order like the floats; NaN wins).
+
+constexpr int kTensorThreads = 256;
+constexpr int kTensorUnroll = 2;
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void* __restrict__ x, int64_t n,
+                                                                      const float* __restrict__ scale_p,
+                                                                      uint32_t* __restrict__ amax_slot,
+                                                                      uint8_t* __restrict__ q) {
+  __shared__ uint32_t red[4];
+  const float s = *scale_p;
+  const int64_t nchunks = n >> 4;
+  const int64_t stride = (int64_t)gridDim.x * kTensorThreads;
+  uint32_t mx = 0;
+  int64_t c = (int64_t)blockIdx.x * kTensorThreads + threadIdx.x;
+  for (; c + (kTensorUnroll - 1) * stride < nchunks; c += kTensorUnroll * stride) {
+    float v[kTensorUnroll][16];
+    uint32_t m[kTensorUnroll];
+#pragma unroll
+    for (int u = 0; u < kTensorUnroll; ++u) {
+      m[u] = 0;
+      load16<BF16>(x, (c + u * stride) << 4, v[u], m[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kTensorUnroll; ++u) {
+      u32x4 o = cast16<FMT>(v[u], s, has_nan<BF16>(m[u]));
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q + ((c + u * stride) << 4)));
+      mx = mx > m[u] ? mx : m[u];
+    }
+  }
+  for (; c < nchunks; c += stride) {
+    float v[16];
+    uint32_t m = 0;
+    load16<BF16>(x, c << 4, v, m);
+    u32x4 o = cast16<FMT>(v, s, has_nan<BF16>(m));
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q + (c << 4)));
+    mx = mx > m ? mx : m;
+  }
+  uint32_t mxf = amax_f32_bits<BF16>(mx);
+  // tail (n % 16 elements): block 0
+  if (blockIdx.x == 0 && threadIdx.x < (n & 15)) {
+    const int64_t i = (nchunks << 4) + threadIdx.x;
+    float xv = load_one<BF16>(x, i);
+    q[i] = cast_one<FMT>(xv, s);
+    uint32_t a = abs_bits(xv);
+    mxf = mxf > a ? mxf : a;
+  }
+  uint32_t r = block_max_u32_256(mxf, red);
+  // a plain read first: most blocks do not raise the running maximum
+  if (threadIdx.x == 0 && amax_slot != nullptr &&
+      r > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    atomicMax(amax_slot, r);
+}
+
+// ------------------------------------------------------------------ 1x128 tiles
+//
+// One 16-lane group per 1x128 run: 8 elements per lane, amax over the group, s = fmax/amax,
+// cast, and scale_inv written at [kb][row] (kb-major, so consecutive rows of one kb are
+// contiguous: a block covers 16 consecutive rows of one kb).
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256) quant_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                         uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
+  const int64_t run = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // run id = kb * rows + row
+  const int64_t nkb = cols >> 7;
+  if (run >= nkb * rows) return;
+  const int64_t kb = run / rows, row = run - kb * rows;
+  const int lane16 = threadIdx.x & 15;
+  const int64_t e0 = row * cols + kb * 128 + lane16 * 8;
+  float v[8];
+  uint32_t mx = 0;
+  if constexpr (BF16) {
+    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
+    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = abs_bits(v[i]);
+    mx = mx > a ? mx : a;
+  }
+  const bool nan_here = mx > 0x7F800000u;
+  mx = group_max_u32<16>(mx);
+  float s, s_inv;
+  current_scale<FMT>(mx, s, s_inv);
+  uint32_t w0 = cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+  uint32_t w1 = cvt4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+  if (nan_here) {
+    w0 = patch_nan4(w0, &v[0]);
+    w1 = patch_nan4(w1, &v[4]);
+  }
+  *reinterpret_cast<uint2*>(q + e0) = make_uint2(w0, w1);
+  if (lane16 == 0) sinv_out[kb * rows + row] = s_inv;
+}
+
+// ------------------------------------------------------------------ 128x128 blocks
+//
+// One 256-thread block per 128x128 block: thread t covers row t/2, columns 64*(t%2)..+64 of
+// the block, held in registers through the block reduction.  A partial last row-block uses
+// the rows present (absent rows contribute nothing).
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256) quant_block_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                          uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
+  __shared__ uint32_t red[4];
+  const int64_t nkb = cols >> 7;
+  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
+  const int64_t row = rb * 128 + (threadIdx.x >> 1);
+  const bool valid = row < rows;
+  const int64_t e0 = row * cols + kb * 128 + (threadIdx.x & 1) * 64;
+  float v[64];
+  uint32_t mx = 0;
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float t[16];
+      load16<BF16>(x, e0 + 16 * c, t, mx);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * c + i] = t[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = 0.0f;
+  }
+  const uint32_t mine = amax_f32_bits<BF16>(mx);
+  const uint32_t bm = block_max_u32_256(mine, red);
+  float s, s_inv;
+  current_scale<FMT>(bm, s, s_inv);
+  if (valid) {
+    const bool nan_here = has_nan<BF16>(mx);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] = v[16 * c + i];
+      u32x4 o = cast16<FMT>(t, s, nan_here);
+      *reinterpret_cast<u32x4*>(q + e0 + 16 * c) = o;
+    }
+  }
+  if (threadIdx.x == 0) sinv_out[rb * nkb + kb] = s_inv;
+}
+
+// ------------------------------------------------------------------ MX 1x32
+//
+// One 4-lane group per 1x32 run (8 elements per lane).  E = smallest integer with
+// amax <= fmax * 2^E, from amax's exponent e and mantissa: E = e - bias when the mantissa
+// is <= 1.75 (bits <= 0x600000), else e - bias + 1 (bias 8 for E4M3, 15 for E5M2); clamped
+// to [-127, 127]; zero amax -> -127; non-finite amax -> code 255 and multiplier 1.  The
+// multiplier 2^-E is exact, so the product is rounded only once, by the cast.
+
+template <int FMT>
+__device__ __forceinline__ void mx_rule(uint32_t amax_bits, uint32_t& code, float& mult) {
+  if (amax_bits >= 0x7F800000u) {
+    code = 255u;
+    mult = 1.0f;
+    return;
+  }
+  int E;
+  const int ef = (int)(amax_bits >> 23);
+  if (ef == 0) {
+    E = -127;  // zero or subnormal amax: the smallest E already exceeds it
+  } else {
+    const int e = ef - 127;
+    E = e - Fp8Traits<FMT>::mx_bias + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  }
+  code = (uint32_t)(E + 127);
+  // E <= 120 for every finite amax, so 2^-E is a normal float: exponent field 127 - E
+  mult = __uint_as_float((uint32_t)(127 - E) << 23);
+}
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
+  const int64_t ngroups = rows * (cols >> 5);
+  const int64_t g = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  if (g >= ngroups) return;
+  const int lane4 = threadIdx.x & 3;
+  const int64_t e0 = g * 32 + lane4 * 8;  // groups are consecutive runs of 32 in row-major order
+  float v[8];
+  if constexpr (BF16) {
+    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
+    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = abs_bits(v[i]);
+    mx = mx > a ? mx : a;
+  }
+  const bool nan_here = mx > 0x7F800000u;
+  mx = group_max_u32<4>(mx);
+  uint32_t code;
+  float mult;
+  mx_rule<FMT>(mx, code, mult);
+  uint32_t w0 = cvt4<FMT>(v[0] * mult, v[1] * mult, v[2] * mult, v[3] * mult);
+  uint32_t w1 = cvt4<FMT>(v[4] * mult, v[5] * mult, v[6] * mult, v[7] * mult);
+  if (nan_here) {
+    w0 = patch_nan4(w0, &v[0]);
+    w1 = patch_nan4(w1, &v[4]);
+  }
+  *reinterpret_cast<uint2*>(q + e0) = make_uint2(w0, w1);
+  if (lane4 == 0) e8[g] = (uint8_t)code;
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int FMT, bool BF16>
+static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, const float* scale, float* amax_slot,
+                        uint8_t* q, void* sinv, hipStream_t st) {
+  const int64_t n = rows * cols;
+  if (gran == FP8_SCALE_TENSOR) {
+    const int64_t nchunks = n >> 4;
+    int64_t blocks = (nchunks + kTensorThreads * kTensorUnroll - 1) / (kTensorThreads * kTensorUnroll);
+    if (blocks < 1) blocks = 1;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL((quant_tensor_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(kTensorThreads), 0, st, x, n,
+                       scale, reinterpret_cast<uint32_t*>(amax_slot), q);
+  } else if (gran == FP8_SCALE_TILE_1x128) {
+    const int64_t runs = rows * (cols >> 7);
+    hipLaunchKernelGGL((quant_tile_kernel<FMT, BF16>), dim3((unsigned)((runs + 15) / 16)), dim3(256), 0, st, x, rows,
+                       cols, q, static_cast<float*>(sinv));
+  } else if (gran == FP8_SCALE_BLOCK_128x128) {
+    const int64_t blocks = ((rows + 127) / 128) * (cols >> 7);
+    hipLaunchKernelGGL((quant_block_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
+                       static_cast<float*>(sinv));
+  } else {
+    const int64_t groups = rows * (cols >> 5);
+    hipLaunchKernelGGL((quant_mx_kernel<FMT, BF16>), dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st, x, rows,
+                       cols, q, static_cast<uint8_t*>(sinv));
+  }
+  return check_launch("fp8_quantize");
+}
+
+}  // namespace sfp8
+
+using namespace sfp8;
+
+extern "C" int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int fmt, int granularity,
+                            const float* scale, float* amax_slot, uint8_t* q, void* scale_inv_out, void* stream) {
+  SFP8_REQUIRE(rows >= 0 && cols >= 0, FP8_ERR_SHAPE, "fp8_quantize: negative shape (%lld, %lld)", (long long)rows,
+               (long long)cols);
+  SFP8_REQUIRE(x_dtype == HP_F32 || x_dtype == HP_BF16, FP8_ERR_DTYPE, "fp8_quantize: x_dtype %d", x_dtype);
+  SFP8_REQUIRE(fmt == FP8_E4M3 || fmt == FP8_E5M2, FP8_ERR_ARG, "fp8_quantize: fmt %d", fmt);
+  SFP8_REQUIRE(granularity >= FP8_SCALE_TENSOR && granularity <= FP8_SCALE_MX_1x32, FP8_ERR_ARG,
+               "fp8_quantize: granularity %d", granularity);
+  if (granularity == FP8_SCALE_TENSOR) {
+    SFP8_REQUIRE(scale != nullptr, FP8_ERR_ARG, "fp8_quantize: per-tensor scaling needs the device scale");
+    SFP8_REQUIRE(scale_inv_out == nullptr, FP8_ERR_ARG, "fp8_quantize: per-tensor scaling writes no scale_inv");
+    SFP8_REQUIRE(aligned4(scale) && (amax_slot == nullptr || aligned4(amax_slot)), FP8_ERR_ARG,
+                 "fp8_quantize: scale / amax_slot must be 4-byte aligned");
+  } else {
+    SFP8_REQUIRE(scale == nullptr && amax_slot == nullptr, FP8_ERR_ARG,
+                 "fp8_quantize: current-scaling granularities take no scale / amax_slot");
+    const int64_t run = granularity == FP8_SCALE_MX_1x32 ? 32 : 128;
+    SFP8_REQUIRE(cols % run == 0, FP8_ERR_SHAPE, "fp8_quantize: cols=%lld must be a multiple of %lld",
+                 (long long)cols, (long long)run);
+    SFP8_REQUIRE(rows * cols == 0 || scale_inv_out != nullptr, FP8_ERR_ARG, "fp8_quantize: scale_inv_out is null");
+    SFP8_REQUIRE(granularity == FP8_SCALE_MX_1x32 || scale_inv_out == nullptr || aligned4(scale_inv_out), FP8_ERR_ARG,
+                 "fp8_quantize: scale_inv_out must be 4-byte aligned");
+  }
+  if (rows * cols == 0) return FP8_OK;
+  SFP8_REQUIRE(x != nullptr && q != nullptr, FP8_ERR_ARG, "fp8_quantize: null x or q");
+  SFP8_REQUIRE(aligned16(x) && aligned16(q), FP8_ERR_ARG, "fp8_quantize: x and q must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = x_dtype == HP_BF16;
+  if (fmt == FP8_E4M3)
+    return bf ? launch_quant<FP8_E4M3, true>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st)
+              : launch_quant<FP8_E4M3, false>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st);
+  return bf ? launch_quant<FP8_E5M2, true>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st)
+            : launch_quant<FP8_E5M2, false>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st);
+}

@@ -1,0 +1,145 @@
+"""GPU parity of fp8_gemm against the fp64 oracle, within the bound derived from the
+matrix cores' accumulation (see gpu_util.gemm_bound); exact pins where the result is exact."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import DEV, announce, check_gemm, np_of  # noqa: E402
+from oracle import fp8 as ofp8, gemm as og, quantize as oq  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import scaled_quantize_gemm_amd as m
+
+    return m
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _codes(rng, shape, fmt, realistic=True):
+    """FP8 codes: quantised Gaussian data (realistic) or uniform over all finite codes."""
+    if realistic:
+        x = rng.standard_normal(shape).astype(np.float32)
+        return oq.quantize_tensor(x, np.float32(ofp8.FMAX[fmt] / np.abs(x).max()), fmt)[0]
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    c[~np.isfinite(ofp8.decode(c, fmt))] = 0
+    return c
+
+
+def _scal(v):
+    return torch.tensor([v], dtype=torch.float32, device=DEV)
+
+
+def test_hundred_threes_is_exactly_300(sq):
+    """Course page accumulation example as a GEMM: fp32 promotion gives exactly 300 (not 64)."""
+    announce("100 threes")
+    A = np.zeros((1, 128), np.uint8)
+    A[0, :100] = 0x44  # 3.0
+    B = np.full((1, 128), 0x38, np.uint8)  # 1.0
+    C = sq.fp8_gemm(_t(A), 0, _scal(1.0), 0, _t(B), 0, _scal(1.0), 0, sq.OUT_F32)
+    torch.cuda.synchronize()
+    assert np_of(C)[0, 0] == 300.0
+
+
+def test_bf16_epilogue_rounds_to_nearest_even(sq):
+    """Course page precision paragraph: 257 -> 256 in bf16 (ties to even); 259 -> 260."""
+    announce("bf16 epilogue 257")
+    A = np.zeros((4, 128), np.uint8)
+    B = np.zeros((1, 128), np.uint8)
+    B[0, :] = 0x38  # 1.0
+    # row sums: 256 + 1 = 257, 256 + 3 = 259, -(256 + 1), 255
+    A[0, 0], A[0, 8] = 0x78, 0x38  # 256 in E4M3 = 0x78, then 1.0 in another run of 8
+    A[1, 0], A[1, 8] = 0x78, 0x44  # 256 + 3
+    A[2, 0], A[2, 8] = 0xF8, 0xB8  # -256 - 1
+    A[3, 0], A[3, 8] = 0x78, 0xB8  # 256 - 1 = 255
+    C = sq.fp8_gemm(_t(A), 0, _scal(1.0), 0, _t(B), 0, _scal(1.0), 0, sq.OUT_BF16)
+    torch.cuda.synchronize()
+    assert np_of(C)[:, 0].tolist() == [256.0, 260.0, -256.0, 255.0]
+
+
+def test_accumulator_runs_of_eight(sq):
+    """The matrix-core behaviour the tolerance relies on: a small product in the same run of 8
+    as a large one keeps only bits down to 2^(E-13) (E = the run's largest operand-exponent
+    sum); in another run it is added in fp32."""
+    announce("accumulator model")
+    A = np.zeros((2, 128), np.uint8)
+    B = np.zeros((1, 128), np.uint8)
+    B[0, :] = 0x7E  # 448
+    A[:, 0] = 0x7E  # 448 * 448 = 200704 (exponent sum 16)
+    A[0, 1] = 0x20  # 2^-3 * 448 = 56 -> same run: bits below 2^3 truncated -> 56 kept
+    A[1, 9] = 0x20  # other run -> exact in fp32
+    A[0, 2] = 0x01  # 2^-9 * 448 = 0.875 -> same run -> lost
+    A[1, 10] = 0x01  # other run -> kept (fp32 spacing at 2^17 is 2^-6)
+    C = np_of(sq.fp8_gemm(_t(A), 0, _scal(1.0), 0, _t(B), 0, _scal(1.0), 0, sq.OUT_F32))[:, 0]
+    torch.cuda.synchronize()
+    assert C[0] == 200704.0 + 56.0
+    assert C[1] == 200704.0 + 56.0 + 0.875
+    Cr, S, G = og.gemm_ref(A, 0, np.float32(1), og.TENSOR, B, 0, np.float32(1), og.TENSOR)
+    check_gemm(C[:, None], Cr, S, G, 128, "tensor", False, "accumulator model")
+
+
+def test_k_zero_gives_zero(sq):
+    announce("K = 0")
+    A = torch.empty((5, 0), dtype=torch.uint8, device=DEV)
+    B = torch.empty((7, 0), dtype=torch.uint8, device=DEV)
+    C = sq.fp8_gemm(A, 0, _scal(2.0), 0, B, 0, _scal(3.0), 0, sq.OUT_F32)
+    torch.cuda.synchronize()
+    assert np.all(np_of(C) == 0)
+
+
+TENSOR_CASES = [(256, 256, 256), (200, 300, 384), (1, 1, 128), (130, 70, 128), (33, 517, 256), (512, 384, 1024)]
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1)])
+@pytest.mark.parametrize("out", [0, 1])
+@pytest.mark.parametrize("mnk", TENSOR_CASES)
+def test_tensor_scaled_gemm(sq, fa, fb, out, mnk):
+    M, N, K = mnk
+    announce("tensor gemm", fa, fb, out, mnk)
+    rng = np.random.default_rng(M * 7 + N * 3 + K + fa * 5 + fb * 11)
+    for realistic in (True, False):
+        A, B = _codes(rng, (M, K), fa, realistic), _codes(rng, (N, K), fb, realistic)
+        sa, sb = np.float32(rng.uniform(0.001, 0.1)), np.float32(rng.uniform(0.001, 0.1))
+        C = sq.fp8_gemm(_t(A), fa, _scal(sa), 0, _t(B), fb, _scal(sb), 0, out)
+        torch.cuda.synchronize()
+        Cr, S, G = og.gemm_ref(A, fa, sa, og.TENSOR, B, fb, sb, og.TENSOR)
+        check_gemm(np_of(C), Cr, S, G, K, "tensor", out == 1, f"tensor {mnk} {fa}{fb} out{out} real={realistic}")
+
+
+@pytest.mark.parametrize("out", [0, 1])
+@pytest.mark.parametrize("mnk", [(256, 256, 256), (200, 300, 512), (1, 130, 128), (129, 257, 384)])
+def test_blockwise_gemm(sq, out, mnk):
+    M, N, K = mnk
+    announce("blockwise gemm", out, mnk)
+    rng = np.random.default_rng(M + 13 * N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp2(rng.integers(-6, 6, (M, 1))).astype(np.float32)
+    x.flat[rng.integers(0, x.size, max(1, x.size // 1000))] *= 100.0
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A, sa = oq.quantize_tile_1x128(x, 0)
+    B, sb = oq.quantize_block_128x128(w, 0)
+    C = sq.fp8_gemm(_t(A), 0, _t(sa), sq.FP8_SCALE_TILE_1x128, _t(B), 0, _t(sb), sq.FP8_SCALE_BLOCK_128x128, out)
+    torch.cuda.synchronize()
+    Cr, S, G = og.gemm_ref(A, 0, sa, og.TILE_1x128, B, 0, sb, og.BLOCK_128x128)
+    check_gemm(np_of(C), Cr, S, G, K, "block", out == 1, f"blockwise {mnk} out{out}")
+
+
+@pytest.mark.parametrize("out", [0, 1])
+@pytest.mark.parametrize("mnk", [(256, 256, 256), (100, 200, 384), (1, 1, 128), (257, 129, 512)])
+def test_mx_gemm(sq, out, mnk):
+    M, N, K = mnk
+    announce("mx gemm", out, mnk)
+    rng = np.random.default_rng(M + 17 * N + K)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-30, 30, (M, K // 32)).repeat(32, 1))).astype(np.float32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    A, ea = oq.quantize_mx_1x32(x, 0)
+    B, eb = oq.quantize_mx_1x32(w, 0)
+    C = sq.fp8_gemm(_t(A), 0, _t(ea), sq.FP8_SCALE_MX_1x32, _t(B), 0, _t(eb), sq.FP8_SCALE_MX_1x32, out)
+    torch.cuda.synchronize()
+    Cr, S, G = og.gemm_ref(A, 0, ea, og.MX_1x32, B, 0, eb, og.MX_1x32)
+    check_gemm(np_of(C), Cr, S, G, K, "mx", out == 1, f"mx {mnk} out{out}")

@@ -1,0 +1,159 @@
+"""GPU parity of the quantizers against the oracle: codes, amax and scales bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import DEV, announce, assert_codes_equal, assert_f32_bits_equal, f32_np, np_of  # noqa: E402
+from oracle import fp8 as ofp8, quantize as oq, recipe as orc  # noqa: E402
+
+FMTS = [ofp8.E4M3, ofp8.E5M2]
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import scaled_quantize_gemm_amd as m
+
+    ok, why = m.fp8_device_check(0)
+    assert ok, why
+    return m
+
+
+def _special_f32(n, seed):
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    sp = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001,
+                   0x00000001, 0x80000001, 0x43E00000, 0xC3E00000, 0x43E80000, 0x47600000, 0x47700000],
+                  dtype=np.uint32)
+    k = min(n, len(sp))
+    u[:k] = sp[:k]
+    return u.view(np.float32)
+
+
+def _tensor_quant(sq, x_t, scale, fmt):
+    s = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    slot = torch.zeros(1, dtype=torch.float32, device=DEV)
+    q, _ = sq.fp8_quantize(x_t, fmt, sq.FP8_SCALE_TENSOR, scale=s, amax_slot=slot)
+    torch.cuda.synchronize()
+    return np_of(q), np_of(slot)[0]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tensor_cast_every_bf16_pattern(sq, fmt):
+    """All 65536 bf16 inputs x several scales, incl. NaN / inf / subnormal / -0 / overflow."""
+    bits = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    xb = torch.from_numpy(bits.copy()).to(torch.bfloat16).view(256, 256)
+    for scale in [1.0, float(np.float32(448.0) / np.float32(240.0)), 2.0 ** -10, 3.0e4, 3.4e38]:
+        announce("tensor cast bf16 patterns", ofp8.fmt_name(fmt), scale)
+        q, amax = _tensor_quant(sq, xb.to(DEV), scale, fmt)
+        oq_, oa = oq.quantize_tensor(f32_np(xb), np.float32(scale), fmt)
+        assert_codes_equal(q, oq_, f"bf16 patterns scale={scale}")
+        assert np.isnan(amax) and np.isnan(oa)
+    finite = bits[np.isfinite(bits)]
+    xf = torch.from_numpy(finite.copy()).to(torch.bfloat16)
+    q, amax = _tensor_quant(sq, xf.to(DEV), 1.0, fmt)
+    oq_, oa = oq.quantize_tensor(f32_np(xf), np.float32(1.0), fmt)
+    assert_codes_equal(q, oq_, "finite bf16")
+    assert_f32_bits_equal([amax], [oa], "amax")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 4096 + 7, 1_000_003])
+def test_tensor_cast_random_f32_bits_ragged(sq, fmt, n):
+    announce("tensor cast random f32", ofp8.fmt_name(fmt), n)
+    x = _special_f32(n, 100 + n)
+    for scale in [1.0, 0.37, 1.0e3]:
+        q, amax = _tensor_quant(sq, torch.from_numpy(x.copy()).to(DEV), scale, fmt)
+        oq_, oa = oq.quantize_tensor(x, np.float32(scale), fmt)
+        assert_codes_equal(q, oq_, f"n={n} scale={scale}")
+        assert_f32_bits_equal([amax], [oa], "amax")
+    # finite data: amax bit-exact; amax slot accumulates with max across calls
+    xf = np.where(np.isfinite(x), x, 1.0).astype(np.float32)
+    s = torch.tensor([2.0], dtype=torch.float32, device=DEV)
+    slot = torch.full((1,), 1e-3, dtype=torch.float32, device=DEV)
+    sq.fp8_quantize(torch.from_numpy(xf).to(DEV), fmt, sq.FP8_SCALE_TENSOR, scale=s, amax_slot=slot)
+    sq.fp8_quantize(torch.from_numpy(xf * 0.5).to(DEV), fmt, sq.FP8_SCALE_TENSOR, scale=s, amax_slot=slot)
+    torch.cuda.synchronize()
+    assert_f32_bits_equal(np_of(slot), [max(np.float32(1e-3), orc.amax(xf))], "running amax")
+
+
+def _blocky_data(rows, cols, seed, specials=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-20, 20, (rows, 1))).astype(np.float32)
+    if rows > 2 and cols >= 256:
+        x[1, :] = 0.0  # a zero row: unit scales
+        x[2, 5] *= 1000.0  # an outlier
+    if specials and rows > 4 and cols >= 256:
+        x[3, 7] = np.nan
+        x[4, 130] = np.inf
+        x[0, 3] = -0.0
+        x[0, 200] = 1e-41
+    return x
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("shape", [(1, 128), (37, 384), (256, 1024), (300, 7168)])
+def test_tile_1x128(sq, fmt, bf16, shape):
+    announce("tile 1x128", ofp8.fmt_name(fmt), "bf16" if bf16 else "f32", shape)
+    x = _blocky_data(*shape, seed=shape[0] + 7 * shape[1])
+    xt = torch.from_numpy(x)
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+    q, sinv = sq.fp8_quantize(xt.to(DEV), fmt, sq.FP8_SCALE_TILE_1x128)
+    torch.cuda.synchronize()
+    oq_, osinv = oq.quantize_tile_1x128(f32_np(xt), fmt)
+    assert_codes_equal(np_of(q), oq_, "tile codes")
+    assert_f32_bits_equal(np_of(sinv), osinv, "tile scale_inv")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("shape", [(1, 128), (128, 128), (200, 256), (513, 384)])
+def test_block_128x128(sq, fmt, bf16, shape):
+    announce("block 128x128", ofp8.fmt_name(fmt), "bf16" if bf16 else "f32", shape)
+    x = _blocky_data(*shape, seed=3 * shape[0] + shape[1])
+    xt = torch.from_numpy(x)
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+    q, sinv = sq.fp8_quantize(xt.to(DEV), fmt, sq.FP8_SCALE_BLOCK_128x128)
+    torch.cuda.synchronize()
+    oq_, osinv = oq.quantize_block_128x128(f32_np(xt), fmt)
+    assert_codes_equal(np_of(q), oq_, "block codes")
+    assert_f32_bits_equal(np_of(sinv), osinv, "block scale_inv")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("shape", [(1, 32), (5, 96), (64, 1024), (333, 160)])
+def test_mx_1x32(sq, fmt, bf16, shape):
+    announce("mx 1x32", ofp8.fmt_name(fmt), "bf16" if bf16 else "f32", shape)
+    rng = np.random.default_rng(shape[0] * 31 + shape[1])
+    x = (rng.standard_normal(shape) * np.exp2(rng.integers(-60, 60, (shape[0], shape[1] // 32)).repeat(32, 1)))
+    x = x.astype(np.float32)
+    if shape[0] > 3 and shape[1] >= 96:
+        x[0, :32] = 0.0
+        x[1, 40] = np.nan
+        x[2, 70] = -np.inf
+        x[3, 0] = 1e-40
+    xt = torch.from_numpy(x)
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+    q, e8 = sq.fp8_quantize(xt.to(DEV), fmt, sq.FP8_SCALE_MX_1x32)
+    torch.cuda.synchronize()
+    oq_, oe8 = oq.quantize_mx_1x32(f32_np(xt), fmt)
+    assert_codes_equal(np_of(e8), oe8, "e8m0 codes")
+    assert_codes_equal(np_of(q), oq_, "mx codes")
+
+
+def test_empty_inputs(sq):
+    announce("empty inputs")
+    s = torch.ones(1, device=DEV)
+    q, _ = sq.fp8_quantize(torch.empty((0, 128), device=DEV), sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=s)
+    assert q.shape == (0, 128)
+    q, si = sq.fp8_quantize(torch.empty((0, 128), device=DEV), sq.FP8_E4M3, sq.FP8_SCALE_TILE_1x128)
+    torch.cuda.synchronize()
+    assert q.numel() == 0

@@ -138,7 +138,8 @@ def test_hundred_threes_gemm_is_300():
     A[0, :100] = 0x44
     B = np.full((1, 128), 0x38, np.uint8)
     C, S, G = gemm.gemm_ref(A, E4M3, f32(1), gemm.TENSOR, B, E4M3, f32(1), gemm.TENSOR)
-    assert C[0, 0] == 300.0 and S[0, 0] == 300.0 and G[0, 0] == 12 * 3.0 + 3.0
+    # G: 13 runs holding threes (2^1 * 2^0 each) + 3 runs of zero codes (2^-6 * 2^0 each)
+    assert C[0, 0] == 300.0 and S[0, 0] == 300.0 and G[0, 0] == 13 * 2.0 + 3 * 2.0 ** -6
 
 
 def test_gemm_closed_forms():
@@ -189,15 +190,24 @@ def test_gemm_brute_force_fractions(mode):
             assert abs(Fraction(S[m, n]) - smag) <= smag * Fraction(1, 2 ** 50)
 
 
-def test_group_max_bound_dominates_group_products():
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3)])
+def test_group_exponent_bound_brackets_group_products(fa, fb):
+    """4 G >= sum over runs of 8 of the largest |product|; G <= sum of max|a| max|b| (normal codes)."""
     rng = np.random.default_rng(12)
-    A, B = _codes(rng, (4, 128), E4M3), _codes(rng, (6, 128), E4M3)
-    C, S, G = gemm.gemm_ref(A, E4M3, f32(1), gemm.TENSOR, B, E4M3, f32(1), gemm.TENSOR)
-    a, b = fp8.decode(A, E4M3), fp8.decode(B, E4M3)
+    A, B = _codes(rng, (4, 128), fa), _codes(rng, (6, 128), fb)
+    sa, sb = f32(0.75), f32(3.0)
+    C, S, G = gemm.gemm_ref(A, fa, sa, gemm.TENSOR, B, fb, sb, gemm.TENSOR)
+    a, b = fp8.decode(A, fa) * float(sa), fp8.decode(B, fb) * float(sb)
     for m in range(4):
         for n in range(6):
             p = np.abs(a[m] * b[n]).reshape(16, 8)
-            assert G[m, n] >= p.max(axis=1).sum() and S[m, n] >= abs(C[m, n])
+            assert 4 * G[m, n] >= p.max(axis=1).sum() and S[m, n] >= abs(C[m, n])
+    # exact binades of normal codes: G equals the brute-force sum of run maxima of 2^e
+    An = np.full((1, 128), 0x38, np.uint8)
+    An[0, 5] = 0x50  # 2^3 in E4M3
+    Bn = np.full((1, 128), 0x40, np.uint8)  # 2.0
+    _, _, G1 = gemm.gemm_ref(An, E4M3, f32(1), gemm.TENSOR, Bn, E4M3, f32(1), gemm.TENSOR)
+    assert G1[0, 0] == 8 * 2 + 15 * 2
 
 
 def test_gemm_subset_rows_cols():
