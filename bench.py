@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 scaled-linear hot path on one MI355X.
+
+Workload (the configuration the headline metric is quoted on): MX-style E4M3 with 1x32
+e8m0 scales, A and B [8192 x 8192] bf16 ~N(0,1), square GEMM 8192^3 with bf16 output,
+plus a standalone per-tensor (delayed-scaling) amax + cast of a 2^28-element bf16 tensor.
+
+One step = the whole path once over that batch, inputs resident in HBM:
+  1. fp8_quantize(T, TENSOR)       amax + saturating cast of 2^28 bf16 -> E4M3 (delayed scale)
+  2. fp8_recipe_update             history roll + scale derivation for the stream's slot
+  3. fp8_quantize(A, MX_1x32)      amax per 32 -> e8m0 -> cast
+  4. fp8_quantize(B, MX_1x32)
+  5. fp8_gemm(MX x MX, bf16 out)   scaled-MFMA GEMM 8192^3
+
+Printed: one JSON line.  value = the step's GEMM FLOPs / step time (TFLOP/s, the whole
+step, casts included); per-kernel figures from HIP events on the launch stream over the
+timed region; roofline of the dominant kernel (the GEMM, against dense FP8 MFMA peak)
+and of the amax + cast stream (against HBM peak); the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mx_8192_traffic.json")
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "scaled_quantize_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("source_sha") != _src_hash(*sources):
+        return None
+    return e.get("traffic_bytes")
+
+
+def cpu_baseline(M=8192, K=8192, numel=1 << 28, rows=3072, stream_sample=1 << 26):
+    """The oracle as it stands, on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import workloads
+    from oracle import gemm as og, quantize as oq
+
+    A, B = workloads.w5_inputs()
+    a = A[:rows].float().numpy()
+    b = B[:rows].float().numpy()
+    t = workloads.w5_stream(numel=stream_sample).float().numpy()
+    del A, B
+    t0 = time.perf_counter()
+    qa, ea = oq.quantize_mx_1x32(a, 0)
+    qb, eb = oq.quantize_mx_1x32(b, 0)
+    C, _, _ = og.gemm_ref(qa, 0, ea, og.MX_1x32, qb, 0, eb, og.MX_1x32)
+    C16 = og.to_bf16(C.astype(np.float32))
+    oq.quantize_tensor(t, np.float32(448.0 / 5.5), 0)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * rows * K
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(blas) if blas else 1),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": (f"MX quantize of A[:{rows}] and B[:{rows}] (8192 columns), fp64 GEMM {rows}x{rows}x{K} "
+                       f"with bf16 rounding, per-tensor cast of {stream_sample} stream elements; "
+                       f"value = sample GEMM FLOPs / oracle time"),
+            "host_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "checksum": float(np.abs(C16).sum())}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a device-to-device copy of known size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus N with N > 1 is not supported "
+              "(the quantizers shard rows without communication; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import scaled_quantize_gemm_amd as sq
+    import workloads
+
+    ok, why = sq.fp8_device_check(0)
+    if not ok:
+        raise SystemExit(f"bench.py: {why}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
+        return
+
+    M = N = K = 8192
+    NUMEL = 1 << 28
+    A, B = workloads.w5_inputs()
+    A, B = A.to(dev), B.to(dev)
+    T = workloads.w5_stream().to(dev)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qb = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ea = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    eb = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qt = torch.empty(NUMEL, dtype=torch.uint8, device=dev)
+    st = sq.DelayedScalingState([sq.FP8_E4M3], history_len=16, device=str(dev))
+    scale, amax_slot, _ = st.slot(0)
+
+    names = ["amax_cast_stream", "recipe_update", "mx_quantize_A", "mx_quantize_B", "gemm_mx"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0][0].record()
+        sq.fp8_quantize(T, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=scale, amax_slot=amax_slot, q=qt)
+        if ev is not None:
+            ev[0][1].record()
+            ev[1][0].record()
+        st.update()
+        if ev is not None:
+            ev[1][1].record()
+            ev[2][0].record()
+        sq.fp8_quantize(A, sq.FP8_E4M3, sq.FP8_SCALE_MX_1x32, q=qa, scale_inv_out=ea)
+        if ev is not None:
+            ev[2][1].record()
+            ev[3][0].record()
+        sq.fp8_quantize(B, sq.FP8_E4M3, sq.FP8_SCALE_MX_1x32, q=qb, scale_inv_out=eb)
+        if ev is not None:
+            ev[3][1].record()
+            ev[4][0].record()
+        sq.fp8_gemm(qa, sq.FP8_E4M3, ea, sq.FP8_SCALE_MX_1x32, qb, sq.FP8_E4M3, eb, sq.FP8_SCALE_MX_1x32,
+                    sq.OUT_BF16, C=C)
+        if ev is not None:
+            ev[4][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in names] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    per = {n: sum(events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)) / args.steps
+           for i, n in enumerate(names)}
+
+    gemm_flops = 2.0 * M * N * K
+    stream_bytes = NUMEL * (2 + 1)  # bf16 read + E4M3 write (amax is a scalar)
+    mxq_bytes = M * K * (2 + 1) + M * (K // 32)
+    gemm_tflops = gemm_flops / (per["gemm_mx"] * 1e-3) / 1e12
+    stream_gbs = stream_bytes / (per["amax_cast_stream"] * 1e-3) / 1e9
+    mxq_gbs = mxq_bytes / (per["mx_quantize_A"] * 1e-3) / 1e9
+    value = gemm_flops / (ms_step * 1e-3) / 1e12
+
+    out = {
+        "metric": "FP8 GEMM TFLOP/s (% FP8 MFMA peak) + amax/cast GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "mx_e4m3_square_gemm_8192_plus_amax_cast_2^28", "M": M, "N": N, "K": K,
+                   "scales": "MX 1x32 e8m0 (GEMM); per-tensor delayed, history 16 (stream)",
+                   "in_dtype": "bf16", "out_dtype": "bf16", "stream_numel": NUMEL},
+        "roofline": {"kernel": "gemm_mx", "bound": "mfma", "achieved": round(gemm_tflops, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": _traffic("gemm_mx", ["gemm.hip", "common.h"])},
+        "roofline_amax_cast": {"kernel": "amax_cast_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
+                               "traffic": _traffic("amax_cast_stream", ["quantize.hip", "common.h"])},
+        "kernels_us": {n: round(v * 1e3, 2) for n, v in per.items()},
+        "mx_quantize_gbs": round(mxq_gbs, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
