@@ -129,8 +129,8 @@ def main():
     T = workloads.w5_stream().to(dev)
     qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
     qb = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    ea = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
-    eb = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    ea = torch.empty((K // 32, M), dtype=torch.uint8, device=dev)  # e8m0, [K/32][rows]
+    eb = torch.empty((K // 32, N), dtype=torch.uint8, device=dev)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     qt = torch.empty(NUMEL, dtype=torch.uint8, device=dev)
     st = sq.DelayedScalingState([sq.FP8_E4M3], history_len=16, device=str(dev))

@@ -128,7 +128,9 @@ int fp8_recipe_update(float *amax_history, float *scale, float *scale_inv, const
  *     FP8_SCALE_MX_1x32:  per 1x32 run (cols % 32 == 0): E = smallest integer with
  *                         amax_run <= fmax * 2^E, clamped to [-127, 127]; elements are
  *                         multiplied by 2^-E exactly; scale_inv_out = device uint8
- *                         [rows][cols/32] of e8m0 codes E + 127 (255 if amax is not finite).
+ *                         [cols/32][rows] of e8m0 codes E + 127 (255 if amax is not finite),
+ *                         run-column major like the 1x128 scales, so one K block's scales
+ *                         for consecutive rows are contiguous.
  *     For TILE / BLOCK / MX, scale and amax_slot must be NULL.
  *   Errors: FP8_ERR_ARG, FP8_ERR_SHAPE (cols not a multiple of the run), FP8_ERR_DTYPE.
  */
@@ -163,8 +165,9 @@ int fp8_cast_transpose(const void *x, int x_dtype, int64_t rows, int64_t cols, i
  *                        [ceil(N/128)][K/128]; each 128-long K block's partial sum is
  *                        multiplied by sa[kb][m] * sb[n/128][kb] and added to an fp32
  *                        accumulator (promotion every 128 K).
- *     MX_1x32 x MX_1x32: a_scale_inv = uint8 e8m0 [M][K/32], b_scale_inv = uint8 e8m0
- *                        [N][K/32]; the matrix cores apply 2^(ea + eb) per 32-long run.
+ *     MX_1x32 x MX_1x32: a_scale_inv = uint8 e8m0 [K/32][M], b_scale_inv = uint8 e8m0
+ *                        [K/32][N] (as fp8_quantize writes them); the matrix cores apply
+ *                        2^(ea - 127) * 2^(eb - 127) per 32-long run.
  *   Products are exact; the matrix cores sum runs of 8 products in a fixed-point window
  *   below the run's largest product and promote every run into fp32.
  *   C          device, c_dtype OUT_F32 or OUT_BF16 (round to nearest even), [M][N].

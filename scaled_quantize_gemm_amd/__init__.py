@@ -145,7 +145,7 @@ def fp8_quantize(x: torch.Tensor, fmt: int, granularity: int = FP8_SCALE_TENSOR,
         elif granularity == FP8_SCALE_BLOCK_128x128:
             scale_inv_out = torch.empty(((rows + 127) // 128, cols // 128), dtype=torch.float32, device=x.device)
         else:
-            scale_inv_out = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+            scale_inv_out = torch.empty((cols // 32, rows), dtype=torch.uint8, device=x.device)
     _check(lib.fp8_quantize(_ptr(x), _hp_dtype(x), rows, cols, fmt, granularity, _ptr(scale), _ptr(amax_slot),
                             _ptr(q), _ptr(scale_inv_out), _stream(x)))
     return q, scale_inv_out

@@ -124,18 +124,17 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
     if constexpr (MODE == MODE_MX) {
       const uint8_t* ea = static_cast<const uint8_t*>(sa_p);
       const uint8_t* eb = static_cast<const uint8_t*>(sb_p);
-      const int kq = K / 32;
 #pragma unroll
       for (int i = 0; i < Cfg::TM; ++i) {
         int gm = m0 + wm * Cfg::WM + 16 * i + r;
         gm = gm < M ? gm : M - 1;
-        scale_a[i] = ea[(size_t)gm * kq + 4 * ks + g];
+        scale_a[i] = ea[(size_t)(4 * ks + g) * M + gm];  // e8m0 layout [K/32][M]
       }
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j) {
         int gn = n0 + wn * Cfg::WN + 16 * j + r;
         gn = gn < N ? gn : N - 1;
-        scale_b[j] = eb[(size_t)gn * kq + 4 * ks + g];
+        scale_b[j] = eb[(size_t)(4 * ks + g) * N + gn];
       }
     }
 
@@ -202,9 +201,255 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
     }
 }
 
+// ------------------------------------------------------------------ large-tile kernel
+//
+// 256 x 256 block tile for large problems (per-tensor and MX scaling).  K is staged 64 at a
+// time through NST LDS stages, each filled by direct global -> LDS loads
+// (global_load_lds_dwordx4: lane L's 16 bytes land at the wave's LDS base + 16 L) issued
+// NST-1 stages ahead, so no registers hold tiles in flight.  4 waves in a 2 x 2 grid, each a
+// 128 x 128 wave tile of 4 x 4 v_mfma_*_32x32x64_f8f6f4 (16 fp32 accumulators per tile and
+// lane).  Fragments for stage s+1 are read from LDS while the MFMAs of stage s run.
+//
+// 32x32x64 operand layout: lane l = 32 g + r supplies row r; bytes 0-15 hold K = 16g..16g+15
+// and bytes 16-31 K = 32+16g..; result register e of lane l is C[8(e/4) + 4g + e%4][r]; in the
+// scaled form lane l's e8m0 byte scales row r over K = 32g..32g+31 of the 64-long step.
+//
+// LDS stage: A [256 rows][64 B], B [256][64 B], then (MX) the stage's two K-blocks of e8m0
+// scales for A [2][256] and B [2][256].  16-byte chunk c of a 64-byte row sits at position
+// c ^ ((row >> 1) & 3): the 8 rows one 128-bit read phase touches cover distinct banks.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs (each with its own L2), so
+// block b runs on XCD b % 8; each XCD gets a contiguous range of tiles, walked in groups of
+// 4 tile-rows so that the tiles resident on one XCD share A rows and B columns.
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64;
+constexpr int BIG_TILE_BYTES = (BIG_BM + BIG_BN) * BIG_BK;  // 32 KB
+constexpr int BIG_SCALE_BYTES = 2 * (BIG_BM + BIG_BN);      // 1 KB (MX only)
+constexpr int BIG_NST = 4;
+
+__device__ __forceinline__ int bswz(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 3)) << 4); }
+
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int xcd = b & 7, idx = b >> 3;
+  const int per = T >> 3, rem = T & 7;
+  const int t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  constexpr int GM = 4;
+  const int group = t / (GM * tiles_n);
+  const int first = group * GM;
+  const int gsz = (tiles_m - first) < GM ? (tiles_m - first) : GM;
+  const int in = t - group * GM * tiles_n;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier for the DMA pipeline: this wave's LDS reads are complete (lgkmcnt(0)) and
+// every wave has arrived.  The caller has already waited (vmcnt) for exactly the stage it is
+// about to read; a __syncthreads() fence would also drain every later prefetch in flight.
+// The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MODE, int FA, int FB, int OUT>
+__global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                          const void* __restrict__ sa_p, const void* __restrict__ sb_p,
+                                                          void* __restrict__ C, int M, int N, int K, int tiles_m,
+                                                          int tiles_n) {
+  constexpr int NST = BIG_NST;
+  constexpr bool MX = MODE == MODE_MX;
+  constexpr int STAGE = BIG_TILE_BYTES + (MX ? BIG_SCALE_BYTES : 0);
+  // one LDS array per stage: distinct objects let the compiler see that a DMA into one stage
+  // does not alias fragment reads from another
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[STAGE];
+  static_assert(NST == 4, "the main loop is unrolled for 4 stages");
+  auto stage_buf = [&](int st) -> uint8_t* { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5, r = lane & 31;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
+  const int nk = K / BIG_BK;
+
+  // ---- direct-to-LDS load descriptors: 4 A chunks and 4 B chunks per thread per stage
+  const uint8_t* ga[4];
+  const uint8_t* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (wave * 4 + i) * 64 + lane;
+    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 1) & 3);
+    const int gm = (m0 + row) < M ? (m0 + row) : M - 1;
+    const int gn = (n0 + row) < N ? (n0 + row) : N - 1;
+    ga[i] = A + (size_t)gm * K + c * 16;
+    gb[i] = B + (size_t)gn * K + c * 16;
+  }
+  // MX scales: wave w loads one 256-byte run: w = 0,1 -> A blocks 2s+w; w = 2,3 -> B blocks 2s+w-2
+  const uint8_t* gs = nullptr;
+  if constexpr (MX) {
+    const bool isb = wave >= 2;
+    const int blk = wave & 1, base = isb ? n0 : m0, lim = isb ? N : M;
+    int row = base + lane * 4;
+    row = row + 3 < lim ? row : (lim >= 4 ? lim - 4 : 0);  // 4-byte loads kept inside the row
+    gs = static_cast<const uint8_t*>(isb ? sb_p : sa_p) + (size_t)blk * lim + row;
+  }
+  auto issue = [&](int ks, uint8_t* base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(ga[i] + (size_t)ks * BIG_BK, (lds_ptr_t)(base + (wave * 4 + i) * 1024), 16, 0,
+                                       0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(gb[i] + (size_t)ks * BIG_BK,
+                                       (lds_ptr_t)(base + BIG_BM * BIG_BK + (wave * 4 + i) * 1024), 16, 0, 0);
+    if constexpr (MX) {
+      const int lim = wave >= 2 ? N : M;
+      __builtin_amdgcn_global_load_lds(gs + (size_t)(2 * ks) * lim, (lds_ptr_t)(base + BIG_TILE_BYTES + wave * 256), 4,
+                                       0, 0);
+    }
+  };
+  constexpr int OPS = MX ? 9 : 8;  // vector-memory ops per thread per stage
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  auto frag = [&](const uint8_t* base, int row) -> v8i {
+    u32x4 lo = *reinterpret_cast<const u32x4*>(base + bswz(row, g));
+    u32x4 hi = *reinterpret_cast<const u32x4*>(base + bswz(row, g + 2));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto read_a = [&](const uint8_t* buf, int i) { return frag(buf, wm * 128 + 32 * i + r); };
+  auto read_b = [&](const uint8_t* buf, int j) { return frag(buf + BIG_BM * BIG_BK, wn * 128 + 32 * j + r); };
+
+  // What a stage needs before its first MFMA: all B fragments, A row-tile 0, and (MX) scales.
+  struct Head {
+    v8i b[4];
+    v8i a0;
+    int sa[4], sb[4];
+  };
+  auto read_head = [&](const uint8_t* buf, Head& h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h.b[j] = read_b(buf, j);
+    h.a0 = read_a(buf, 0);
+    if constexpr (MX) {
+      const uint8_t* sbase = buf + BIG_TILE_BYTES;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h.sa[i] = sbase[g * 256 + wm * 128 + 32 * i + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h.sb[j] = sbase[512 + g * 256 + wn * 128 + 32 * j + r];
+    }
+  };
+  auto row = [&](int i, const v8i& a, const Head& h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (MX)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, h.b[j], acc[i][j], FA, FB, 0, h.sa[i], 0,
+                                                                     h.sb[j]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, h.b[j], acc[i][j], FA, FB, 0, 0, 0, 0);
+    }
+  };
+  // wait until at most `later` stages' loads are still in flight (loads retire in order)
+  auto wait_stage = [&](int later) {
+    if (later >= 3) {
+      if constexpr (OPS == 9) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    } else if (later == 2) {
+      if constexpr (OPS == 9) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else if (later == 1) {
+      if constexpr (OPS == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+
+  // Iteration s (its stage in `buf`, head already in `cur`):
+  //   A row-tiles 1..3 are read from LDS while the MFMA rows before them run;
+  //   before the last row: wait for stage s+1 and barrier -- every wave has now finished
+  //   reading stage s, so its buffer is refilled with stage s+NST -- then read the head of
+  //   stage s+1 into `nxt` while the last row of MFMAs runs.
+  auto body = [&](int s, uint8_t* buf, uint8_t* nbuf, Head& cur, Head& nxt) {
+    v8i a1 = read_a(buf, 1);
+    row(0, cur.a0, cur);
+    v8i a2 = read_a(buf, 2);
+    row(1, a1, cur);
+    v8i a3 = read_a(buf, 3);
+    row(2, a2, cur);
+    if (s + 1 < nk) {
+      const int later = (nk - 2 - s) < (NST - 2) ? (nk - 2 - s) : (NST - 2);
+      wait_stage(later);
+      lds_barrier();
+      if (s + NST < nk) issue(s + NST, buf);
+      read_head(nbuf, nxt);
+    }
+    row(3, a3, cur);
+  };
+
+  Head H0, H1;
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+      if (s < nk) issue(s, stage_buf(s));
+    wait_stage(nk - 1 < NST - 1 ? nk - 1 : NST - 1);
+    lds_barrier();
+    read_head(stage_buf(0), H0);
+  }
+  for (int s = 0; s < nk; s += 4) {
+    body(s, lds0, lds1, H0, H1);
+    if (s + 1 < nk) body(s + 1, lds1, lds2, H1, H0);
+    if (s + 2 < nk) body(s + 2, lds2, lds3, H0, H1);
+    if (s + 3 < nk) body(s + 3, lds3, lds0, H1, H0);
+  }
+
+  // ---- epilogue: C[m][n], lane holds rows 8(e/4) + 4g + e%4 of each 32x32 tile, column r
+  float scale = 1.0f;
+  if constexpr (MODE == MODE_TENSOR) scale = *static_cast<const float*>(sa_p) * *static_cast<const float*>(sb_p);
+  const bool full = m0 + BIG_BM <= M && n0 + BIG_BN <= N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + wn * 128 + 32 * j + r;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gm = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+        const float v = MODE == MODE_TENSOR ? acc[i][j][e] * scale : acc[i][j][e];
+        if (full || (gm < M && gn < N)) {
+          if constexpr (OUT == OUT_F32)
+            static_cast<float*>(C)[(size_t)gm * N + gn] = v;
+          else
+            static_cast<uint16_t*>(C)[(size_t)gm * N + gn] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+}
+
 template <int MODE, int FA, int FB, int OUT>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, void* C, int M, int N, int K,
                        hipStream_t st) {
+  if constexpr (MODE != MODE_BLOCK) {
+    const int tiles_m = (M + BIG_BM - 1) / BIG_BM, tiles_n = (N + BIG_BN - 1) / BIG_BN;
+    // large problems only (>= half a wave of tiles on 256 CUs); MX scale rows are read as
+    // 4-byte runs, so M and N must be multiples of 4 there
+    if (tiles_m * tiles_n >= 128 && M >= 4 && N >= 4 && (MODE != MODE_MX || (M % 4 == 0 && N % 4 == 0))) {
+      hipLaunchKernelGGL((gemm_big_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(256), 0, st, A, B, sa, sb,
+                         C, M, N, K, tiles_m, tiles_n);
+      return check_launch("fp8_gemm");
+    }
+  }
   constexpr int BM = 128, BN = 128;
   using Cfg = GemmCfg<BM, BN>;
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);

@@ -292,14 +292,19 @@ __device__ __forceinline__ void mx_rule(uint32_t amax_bits, uint32_t& code, floa
   mult = __uint_as_float((uint32_t)(127 - E) << 23);
 }
 
+// A block covers 16 rows x 4 runs; wave w takes run 4*cb + w of the 16 rows, so the 16 e8m0
+// bytes it writes (layout [cols/32][rows]) are contiguous.
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
-  const int64_t ngroups = rows * (cols >> 5);
-  const int64_t g = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-  if (g >= ngroups) return;
+  const int64_t nrun = cols >> 5;
+  const int64_t ncb = (nrun + 3) >> 2;
+  const int64_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
+  const int64_t run = cb * 4 + (threadIdx.x >> 6);
+  const int64_t row = rb * 16 + ((threadIdx.x >> 2) & 15);
+  if (run >= nrun || row >= rows) return;  // whole 4-lane groups leave together
   const int lane4 = threadIdx.x & 3;
-  const int64_t e0 = g * 32 + lane4 * 8;  // groups are consecutive runs of 32 in row-major order
+  const int64_t e0 = row * cols + run * 32 + lane4 * 8;
   float v[8];
   if constexpr (BF16) {
     u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
@@ -334,7 +339,7 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ 
     w1 = patch_nan4(w1, &v[4]);
   }
   *reinterpret_cast<uint2*>(q + e0) = make_uint2(w0, w1);
-  if (lane4 == 0) e8[g] = (uint8_t)code;
+  if (lane4 == 0) e8[run * rows + row] = (uint8_t)code;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -359,9 +364,9 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
     hipLaunchKernelGGL((quant_block_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
                        static_cast<float*>(sinv));
   } else {
-    const int64_t groups = rows * (cols >> 5);
-    hipLaunchKernelGGL((quant_mx_kernel<FMT, BF16>), dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st, x, rows,
-                       cols, q, static_cast<uint8_t*>(sinv));
+    const int64_t blocks = ((rows + 15) / 16) * (((cols >> 5) + 3) / 4);
+    hipLaunchKernelGGL((quant_mx_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
+                       static_cast<uint8_t*>(sinv));
   }
   return check_launch("fp8_quantize");
 }

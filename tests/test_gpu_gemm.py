@@ -139,7 +139,41 @@ def test_mx_gemm(sq, out, mnk):
     w = rng.standard_normal((N, K)).astype(np.float32)
     A, ea = oq.quantize_mx_1x32(x, 0)
     B, eb = oq.quantize_mx_1x32(w, 0)
-    C = sq.fp8_gemm(_t(A), 0, _t(ea), sq.FP8_SCALE_MX_1x32, _t(B), 0, _t(eb), sq.FP8_SCALE_MX_1x32, out)
+    C = sq.fp8_gemm(_t(A), 0, _t(ea.T), sq.FP8_SCALE_MX_1x32, _t(B), 0, _t(eb.T), sq.FP8_SCALE_MX_1x32, out)
     torch.cuda.synchronize()
     Cr, S, G = og.gemm_ref(A, 0, ea, og.MX_1x32, B, 0, eb, og.MX_1x32)
     check_gemm(np_of(C), Cr, S, G, K, "mx", out == 1, f"mx {mnk} out{out}")
+
+
+# Shapes with >= 128 tiles of 256 x 256 run on the large-tile kernel: ragged edges, K steps
+# fewer than the pipeline depth and not a multiple of it.
+BIG_CASES = [(2048, 4096, 128), (2148, 4036, 384), (4096, 2304, 1152), (2052, 4100, 256)]
+
+
+@pytest.mark.parametrize("mnk", BIG_CASES)
+@pytest.mark.parametrize("mode", ["tensor", "mx"])
+def test_large_tile_kernel(sq, mnk, mode):
+    M, N, K = mnk
+    announce("large-tile gemm", mode, mnk)
+    rng = np.random.default_rng(M + N + K)
+    if mode == "tensor":
+        A, B = _codes(rng, (M, K), 1, True), _codes(rng, (N, K), 0, True)
+        sa, sb = np.float32(0.0123), np.float32(0.0456)
+        C = sq.fp8_gemm(_t(A), 1, _scal(sa), 0, _t(B), 0, _scal(sb), 0, sq.OUT_BF16)
+        torch.cuda.synchronize()
+        r = np.sort(rng.choice(M, 256, replace=False))
+        r[-1] = M - 1
+        Cr, S, G = og.gemm_ref(A, 1, sa, og.TENSOR, B, 0, sb, og.TENSOR, rows=r)
+        check_gemm(np_of(C)[r], Cr, S, G, K, "tensor", True, f"large tensor {mnk}")
+    else:
+        x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-8, 8, (M, K // 32)).repeat(32, 1))).astype(np.float32)
+        w = rng.standard_normal((N, K)).astype(np.float32)
+        A, ea = oq.quantize_mx_1x32(x, 0)
+        B, eb = oq.quantize_mx_1x32(w, 0)
+        C = sq.fp8_gemm(_t(A), 0, _t(ea.T), sq.FP8_SCALE_MX_1x32, _t(B), 0, _t(eb.T), sq.FP8_SCALE_MX_1x32,
+                        sq.OUT_F32)
+        torch.cuda.synchronize()
+        r = np.sort(rng.choice(M, 256, replace=False))
+        r[-1] = M - 1
+        Cr, S, G = og.gemm_ref(A, 0, ea, og.MX_1x32, B, 0, eb, og.MX_1x32, rows=r)
+        check_gemm(np_of(C)[r], Cr, S, G, K, "mx", False, f"large mx {mnk}")

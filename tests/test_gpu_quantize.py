@@ -145,7 +145,7 @@ def test_mx_1x32(sq, fmt, bf16, shape):
     q, e8 = sq.fp8_quantize(xt.to(DEV), fmt, sq.FP8_SCALE_MX_1x32)
     torch.cuda.synchronize()
     oq_, oe8 = oq.quantize_mx_1x32(f32_np(xt), fmt)
-    assert_codes_equal(np_of(e8), oe8, "e8m0 codes")
+    assert_codes_equal(np_of(e8).T, oe8, "e8m0 codes (layout [cols/32][rows])")
     assert_codes_equal(np_of(q), oq_, "mx codes")
 
 
