@@ -21,6 +21,8 @@
 //  * TENSOR:  acc over all K; C = acc * (sa * sb).
 //  * BLOCK:   per 128-K block kb: p = MFMA from zero; acc += p * (sa[kb][m] * sb[n/128][kb]).
 //  * MX:      scaled MFMA with the e8m0 codes of A[m][4kb+g] and B[n][4kb+g]; C = acc.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sfp8 {
@@ -40,8 +42,10 @@ struct GemmCfg {
   static constexpr int LDS_A = BM * BK, LDS_B = BN * BK;  // bytes per stage
 };
 
-// byte offset of 16-byte chunk c of tile row `row` in a 128-byte-row LDS tile
-__device__ __forceinline__ int swz(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+// byte offset of 16-byte chunk c of tile row `row` in a 128-byte-row LDS tile; the position
+// c ^ ((row >> 1) ^ ((row & 1) << 2)) is distinct over any 8 consecutive rows (32 banks) and
+// over 16 consecutive rows for each row parity (64 banks), so fragment reads do not conflict
+__device__ __forceinline__ int swz(int row, int c) { return row * 128 + ((c ^ (((row >> 1) ^ ((row & 1) << 2)) & 7)) << 4); }
 
 template <int BM, int BN, int MODE, int FA, int FB, int OUT>
 __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
@@ -216,7 +220,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
 //
 // LDS stage: A [256 rows][64 B], B [256][64 B], then (MX) the stage's two K-blocks of e8m0
 // scales for A [2][256] and B [2][256].  16-byte chunk c of a 64-byte row sits at position
-// c ^ ((row >> 1) & 3): the 8 rows one 128-bit read phase touches cover distinct banks.
+// c ^ (((row >> 2) ^ (row >> 1)) & 3): the rows one 128-bit read phase touches (8 rows over
+// 32 banks, or 16 rows over 64 banks) then cover distinct banks, and rows 32 apart share it.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs (each with its own L2), so
 // block b runs on XCD b % 8; each XCD gets a contiguous range of tiles, walked in groups of
@@ -229,7 +234,8 @@ constexpr int BIG_TILE_BYTES = (BIG_BM + BIG_BN) * BIG_BK;  // 32 KB
 constexpr int BIG_SCALE_BYTES = 2 * (BIG_BM + BIG_BN);      // 1 KB (MX only)
 constexpr int BIG_NST = 4;
 
-__device__ __forceinline__ int bswz(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 3)) << 4); }
+__device__ __forceinline__ int bswz_pos(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }
+__device__ __forceinline__ int bswz(int row, int c) { return row * 64 + ((c ^ bswz_pos(row)) << 4); }
 
 __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int T = tiles_m * tiles_n;
@@ -251,7 +257,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // every wave has arrived.  The caller has already waited (vmcnt) for exactly the stage it is
 // about to read; a __syncthreads() fence would also drain every later prefetch in flight.
 // The "memory" clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The lgkmcnt(0) wait is the builtin (encoding: vmcnt 63, expcnt 7, lgkmcnt 0) so that the
+// compiler's wait-count tracking knows every LDS read has completed at this point.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int MODE, int FA, int FB, int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
@@ -270,7 +281,8 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
   static_assert(NST == 4, "the main loop is unrolled for 4 stages");
   auto stage_buf = [&](int st) -> uint8_t* { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 5, r = lane & 31;
   int tm, tn;
@@ -278,41 +290,45 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
   const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
   const int nk = K / BIG_BK;
 
-  // ---- direct-to-LDS load descriptors: 4 A chunks and 4 B chunks per thread per stage
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
+  // ---- direct-to-LDS loads: uniform tile bases + 32-bit per-lane offsets (4 A and 4 B chunks
+  //      per thread per stage); rows past the matrix edge re-read its last row
+  const uint8_t* a_base = A + (size_t)m0 * K;
+  const uint8_t* b_base = B + (size_t)n0 * K;
+  uint32_t oa[4], ob[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int slot = (wave * 4 + i) * 64 + lane;
-    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 1) & 3);
-    const int gm = (m0 + row) < M ? (m0 + row) : M - 1;
-    const int gn = (n0 + row) < N ? (n0 + row) : N - 1;
-    ga[i] = A + (size_t)gm * K + c * 16;
-    gb[i] = B + (size_t)gn * K + c * 16;
+    const int row = slot >> 2, c = (slot & 3) ^ bswz_pos(row);
+    const int ra = row < M - m0 ? row : M - 1 - m0;
+    const int rb = row < N - n0 ? row : N - 1 - n0;
+    oa[i] = (uint32_t)ra * (uint32_t)K + c * 16;
+    ob[i] = (uint32_t)rb * (uint32_t)K + c * 16;
   }
-  // MX scales: wave w loads one 256-byte run: w = 0,1 -> A blocks 2s+w; w = 2,3 -> B blocks 2s+w-2
-  const uint8_t* gs = nullptr;
+  // MX scales: wave w loads one 256-row run: w = 0,1 -> A K-blocks 2s+w; w = 2,3 -> B blocks 2s+w-2
+  const uint8_t* s_base = nullptr;
+  uint32_t os = 0;
+  int s_lim = 0;
   if constexpr (MX) {
     const bool isb = wave >= 2;
-    const int blk = wave & 1, base = isb ? n0 : m0, lim = isb ? N : M;
-    int row = base + lane * 4;
-    row = row + 3 < lim ? row : (lim >= 4 ? lim - 4 : 0);  // 4-byte loads kept inside the row
-    gs = static_cast<const uint8_t*>(isb ? sb_p : sa_p) + (size_t)blk * lim + row;
+    s_lim = isb ? N : M;
+    const int base_row = isb ? n0 : m0;
+    s_base = static_cast<const uint8_t*>(isb ? sb_p : sa_p) + (size_t)(wave & 1) * s_lim + base_row;
+    const int rel = lane * 4, room = s_lim - 4 - base_row;  // M, N multiples of 4 here
+    os = (uint32_t)(rel < room ? rel : room);
   }
-  auto issue = [&](int ks, uint8_t* base) {
+  auto issue = [&](int ks, uint8_t* buf) {
+    const uint8_t* ab = a_base + (size_t)ks * BIG_BK;
+    const uint8_t* bb = b_base + (size_t)ks * BIG_BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(ga[i] + (size_t)ks * BIG_BK, (lds_ptr_t)(base + (wave * 4 + i) * 1024), 16, 0,
+      __builtin_amdgcn_global_load_lds(ab + oa[i], (lds_ptr_t)(buf + (wave * 4 + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(bb + ob[i], (lds_ptr_t)(buf + BIG_BM * BIG_BK + (wave * 4 + i) * 1024), 16, 0,
                                        0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(gb[i] + (size_t)ks * BIG_BK,
-                                       (lds_ptr_t)(base + BIG_BM * BIG_BK + (wave * 4 + i) * 1024), 16, 0, 0);
-    if constexpr (MX) {
-      const int lim = wave >= 2 ? N : M;
-      __builtin_amdgcn_global_load_lds(gs + (size_t)(2 * ks) * lim, (lds_ptr_t)(base + BIG_TILE_BYTES + wave * 256), 4,
-                                       0, 0);
-    }
+    if constexpr (MX)
+      __builtin_amdgcn_global_load_lds(s_base + (size_t)(2 * ks) * s_lim + os,
+                                       (lds_ptr_t)(buf + BIG_TILE_BYTES + wave * 256), 4, 0, 0);
   };
   constexpr int OPS = MX ? 9 : 8;  // vector-memory ops per thread per stage
 
@@ -332,16 +348,12 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
   auto read_a = [&](const uint8_t* buf, int i) { return frag(buf, wm * 128 + 32 * i + r); };
   auto read_b = [&](const uint8_t* buf, int j) { return frag(buf + BIG_BM * BIG_BK, wn * 128 + 32 * j + r); };
 
-  // What a stage needs before its first MFMA: all B fragments, A row-tile 0, and (MX) scales.
+  // A stage's operands in registers: A and B fragments and (MX) scales.
   struct Head {
-    v8i b[4];
-    v8i a0;
+    v8i a[4], b[4];
     int sa[4], sb[4];
   };
-  auto read_head = [&](const uint8_t* buf, Head& h) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) h.b[j] = read_b(buf, j);
-    h.a0 = read_a(buf, 0);
+  auto read_scales = [&](const uint8_t* buf, Head& h) {
     if constexpr (MX) {
       const uint8_t* sbase = buf + BIG_TILE_BYTES;
 #pragma unroll
@@ -376,42 +388,88 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
     }
   };
 
-  // Iteration s (its stage in `buf`, head already in `cur`):
-  //   A row-tiles 1..3 are read from LDS while the MFMA rows before them run;
-  //   before the last row: wait for stage s+1 and barrier -- every wave has now finished
-  //   reading stage s, so its buffer is refilled with stage s+NST -- then read the head of
-  //   stage s+1 into `nxt` while the last row of MFMAs runs.
-  auto body = [&](int s, uint8_t* buf, uint8_t* nbuf, Head& cur, Head& nxt) {
-    v8i a1 = read_a(buf, 1);
-    row(0, cur.a0, cur);
-    v8i a2 = read_a(buf, 2);
-    row(1, a1, cur);
-    v8i a3 = read_a(buf, 3);
-    row(2, a2, cur);
-    if (s + 1 < nk) {
-      const int later = (nk - 2 - s) < (NST - 2) ? (nk - 2 - s) : (NST - 2);
-      wait_stage(later);
-      lds_barrier();
-      if (s + NST < nk) issue(s + NST, buf);
-      read_head(nbuf, nxt);
-    }
-    row(3, a3, cur);
+  auto read_part1 = [&](const uint8_t* buf, Head& h) {
+    h.b[0] = read_b(buf, 0);
+    h.b[1] = read_b(buf, 1);
+    h.a[0] = read_a(buf, 0);
+    h.a[1] = read_a(buf, 1);
   };
+  auto read_part2 = [&](const uint8_t* buf, Head& h) {
+    h.b[2] = read_b(buf, 2);
+    h.b[3] = read_b(buf, 3);
+    h.a[2] = read_a(buf, 2);
+    h.a[3] = read_a(buf, 3);
+    read_scales(buf, h);
+  };
+
+  // One pipeline stage s.  On entry (after barrier B_s): stage s's operands are in `cur`, every
+  // wave has finished reading `buf` (stage s), and stage s+1 has landed in `nbuf`.
+  //   refill `buf` with stage s+NST | read stage s+1's operands into `nxt` | 16 MFMAs of
+  //   stage s -- the DMA and LDS reads interleaved between the MFMAs so the matrix core never
+  //   waits on them | wait for stage s+2 and for the reads, barrier B_{s+1}.
+  // STEADY: stages s+1, s+2 and s+NST exist.
+  auto stage = [&](auto steady, int s, uint8_t* buf, uint8_t* nbuf, Head& cur, Head& nxt) {
+    constexpr bool STEADY = decltype(steady)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    if (STEADY || s + NST < nk) issue(s + NST, buf);
+    const bool more = STEADY || s + 1 < nk;
+    if (more) {
+      read_part1(nbuf, nxt);
+      read_part2(nbuf, nxt);
+    }
+    row(0, cur.a[0], cur);
+    row(1, cur.a[1], cur);
+    row(2, cur.a[2], cur);
+    row(3, cur.a[3], cur);
+    // interleave: per MFMA, two LDS reads and one DMA (and the address math they need)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (LDS DMA)
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (STEADY || s + 2 < nk) {
+      if constexpr (STEADY) {
+        wait_stage(NST - 2);
+      } else {
+        const int later = (nk - 3 - s) < (NST - 2) ? (nk - 3 - s) : (NST - 2);
+        wait_stage(later);
+      }
+      lds_barrier();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using steady_t = std::integral_constant<bool, true>;
+  using tail_t = std::integral_constant<bool, false>;
 
   Head H0, H1;
   if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < NST; ++s)
       if (s < nk) issue(s, stage_buf(s));
-    wait_stage(nk - 1 < NST - 1 ? nk - 1 : NST - 1);
+    wait_stage(nk - 1 < NST - 1 ? nk - 1 : NST - 1);  // stage 0 landed
     lds_barrier();
-    read_head(stage_buf(0), H0);
+    read_part1(lds0, H0);
+    read_part2(lds0, H0);
+    if (nk > 1) {
+      wait_stage(nk - 2 < NST - 2 ? nk - 2 : NST - 2);  // stage 1 landed
+      lds_barrier();                                    // B_0: stage 0 fully read by every wave
+    }
   }
-  for (int s = 0; s < nk; s += 4) {
-    body(s, lds0, lds1, H0, H1);
-    if (s + 1 < nk) body(s + 1, lds1, lds2, H1, H0);
-    if (s + 2 < nk) body(s + 2, lds2, lds3, H0, H1);
-    if (s + 3 < nk) body(s + 3, lds3, lds0, H1, H0);
+  int s = 0;
+  // steady state: every stage in this block of 4 has a successor and a refill
+  for (; s + 3 + NST < nk; s += 4) {
+    stage(steady_t{}, s, lds0, lds1, H0, H1);
+    stage(steady_t{}, s + 1, lds1, lds2, H1, H0);
+    stage(steady_t{}, s + 2, lds2, lds3, H0, H1);
+    stage(steady_t{}, s + 3, lds3, lds0, H1, H0);
+  }
+  for (; s < nk; s += 4) {
+    stage(tail_t{}, s, lds0, lds1, H0, H1);
+    if (s + 1 < nk) stage(tail_t{}, s + 1, lds1, lds2, H1, H0);
+    if (s + 2 < nk) stage(tail_t{}, s + 2, lds2, lds3, H0, H1);
+    if (s + 3 < nk) stage(tail_t{}, s + 3, lds3, lds0, H1, H0);
   }
 
   // ---- epilogue: C[m][n], lane holds rows 8(e/4) + 4g + e%4 of each 32x32 tile, column r
