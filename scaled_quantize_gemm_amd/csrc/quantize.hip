@@ -113,7 +113,8 @@ __device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* red)
 // atomic per block (|x| bits of non-negative floats order like the floats; NaN wins).
 
 constexpr int kTensorThreads = 256;
-constexpr int kTensorUnroll = 2;
+constexpr int kTensorUnroll = 1;
+constexpr int64_t kTensorMaxBlocks = 32768;
 
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void* __restrict__ x, int64_t n,
@@ -292,20 +293,19 @@ __device__ __forceinline__ void mx_rule(uint32_t amax_bits, uint32_t& code, floa
   mult = __uint_as_float((uint32_t)(127 - E) << 23);
 }
 
-// A block covers 16 rows x 4 runs; wave w takes run 4*cb + w of the 16 rows, so the 16 e8m0
-// bytes it writes (layout [cols/32][rows]) are contiguous.
-template <int FMT, bool BF16>
-__global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
-  const int64_t nrun = cols >> 5;
-  const int64_t ncb = (nrun + 3) >> 2;
-  const int64_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
-  const int64_t run = cb * 4 + (threadIdx.x >> 6);
-  const int64_t row = rb * 16 + ((threadIdx.x >> 2) & 15);
-  if (run >= nrun || row >= rows) return;  // whole 4-lane groups leave together
-  const int lane4 = threadIdx.x & 3;
-  const int64_t e0 = row * cols + run * 32 + lane4 * 8;
-  float v[8];
+// A block covers 4*kMxRowsPerWave rows x 16 runs (512 columns).  Wave w takes rows
+// w*kMxRowsPerWave.. of the block; on each row its 64 lanes read 512 consecutive elements
+// (4 lanes per run), so every load and code store is a contiguous row segment.  The e8m0
+// codes collect in LDS as [run][row] and leave as contiguous pieces of the [cols/32][rows]
+// layout.  Consecutive blocks walk the input in address order (all column blocks of one
+// row group, then the next group): on 8192 x 8192 bf16 that order measured 32 us against
+// 43 us for the column-block-major order, whose 16 KB row stride crowds few HBM channels.
+constexpr int kMxRowsPerWave = 2;
+constexpr int kMxRows = 4 * kMxRowsPerWave;
+constexpr int kMxRuns = 16;
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, float (&v)[8]) {
   if constexpr (BF16) {
     u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
     uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -321,25 +321,57 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
   }
-  uint32_t mx = 0;
+}
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
+  __shared__ uint8_t codes[kMxRuns][kMxRows];
+  const int64_t nrun = cols >> 5;
+  const int64_t ncb = (nrun + kMxRuns - 1) / kMxRuns;
+  const int64_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrun = lane >> 2, lane4 = lane & 3;
+  const int64_t run = cb * kMxRuns + lrun;
+  const int64_t row0 = rb * kMxRows + wave * kMxRowsPerWave;
+  if (run < nrun) {  // whole 4-lane groups take the same branch
+    const int64_t c0 = run * 32 + lane4 * 8;
+    float v[kMxRowsPerWave][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t a = abs_bits(v[i]);
-    mx = mx > a ? mx : a;
+    for (int j = 0; j < kMxRowsPerWave; ++j)
+      if (row0 + j < rows) load8<BF16>(x, (row0 + j) * cols + c0, v[j]);
+#pragma unroll
+    for (int j = 0; j < kMxRowsPerWave; ++j) {
+      if (row0 + j >= rows) break;
+      uint32_t mx = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t a = abs_bits(v[j][i]);
+        mx = mx > a ? mx : a;
+      }
+      const bool nan_here = mx > 0x7F800000u;
+      mx = group_max_u32<4>(mx);
+      uint32_t code;
+      float mult;
+      mx_rule<FMT>(mx, code, mult);
+      uint32_t w0 = cvt4<FMT>(v[j][0] * mult, v[j][1] * mult, v[j][2] * mult, v[j][3] * mult);
+      uint32_t w1 = cvt4<FMT>(v[j][4] * mult, v[j][5] * mult, v[j][6] * mult, v[j][7] * mult);
+      if (nan_here) {
+        w0 = patch_nan4(w0, &v[j][0]);
+        w1 = patch_nan4(w1, &v[j][4]);
+      }
+      u32x2 o = {w0, w1};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(q + (row0 + j) * cols + c0));
+      if (lane4 == 0) codes[lrun][wave * kMxRowsPerWave + j] = (uint8_t)code;
+    }
   }
-  const bool nan_here = mx > 0x7F800000u;
-  mx = group_max_u32<4>(mx);
-  uint32_t code;
-  float mult;
-  mx_rule<FMT>(mx, code, mult);
-  uint32_t w0 = cvt4<FMT>(v[0] * mult, v[1] * mult, v[2] * mult, v[3] * mult);
-  uint32_t w1 = cvt4<FMT>(v[4] * mult, v[5] * mult, v[6] * mult, v[7] * mult);
-  if (nan_here) {
-    w0 = patch_nan4(w0, &v[0]);
-    w1 = patch_nan4(w1, &v[4]);
+  __syncthreads();
+  const int64_t rbase = rb * kMxRows;
+  for (int i = threadIdx.x; i < kMxRuns * kMxRows; i += 256) {
+    const int lr = i / kMxRows, rr = i - lr * kMxRows;
+    const int64_t rn = cb * kMxRuns + lr;
+    if (rn < nrun && rbase + rr < rows) e8[rn * rows + rbase + rr] = codes[lr][rr];
   }
-  *reinterpret_cast<uint2*>(q + e0) = make_uint2(w0, w1);
-  if (lane4 == 0) e8[run * rows + row] = (uint8_t)code;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -352,7 +384,7 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
     const int64_t nchunks = n >> 4;
     int64_t blocks = (nchunks + kTensorThreads * kTensorUnroll - 1) / (kTensorThreads * kTensorUnroll);
     if (blocks < 1) blocks = 1;
-    if (blocks > 2048) blocks = 2048;
+    if (blocks > kTensorMaxBlocks) blocks = kTensorMaxBlocks;
     hipLaunchKernelGGL((quant_tensor_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(kTensorThreads), 0, st, x, n,
                        scale, reinterpret_cast<uint32_t*>(amax_slot), q);
   } else if (gran == FP8_SCALE_TILE_1x128) {
@@ -364,7 +396,7 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
     hipLaunchKernelGGL((quant_block_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
                        static_cast<float*>(sinv));
   } else {
-    const int64_t blocks = ((rows + 15) / 16) * (((cols >> 5) + 3) / 4);
+    const int64_t blocks = ((rows + kMxRows - 1) / kMxRows) * (((cols >> 5) + kMxRuns - 1) / kMxRuns);
     hipLaunchKernelGGL((quant_mx_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
                        static_cast<uint8_t*>(sinv));
   }
