@@ -495,6 +495,273 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
     }
 }
 
+// ------------------------------------------------------------------ ping-pong large-tile kernel
+//
+// Same 256 x 256 block tile, K step 64 and 4-stage LDS ring fed by direct-to-LDS loads as
+// above, but 8 waves in two groups of 4.  Group p computes tile rows 128p .. 128p+127; wave i
+// of a group computes tile columns 64i .. 64i+63 (a 128 x 64 wave tile: 4 x 2 MFMAs of
+// 32x32x64 per K step, 128 fp32 accumulators per lane).  Waves w and w+4 share a SIMD.
+//
+// Every wave runs the same sequence M_0 C_0 M_1 C_1 ... of memory phases (issue this wave's
+// part of stage k+3, read stage k's fragments from LDS) and compute phases (8 MFMAs on
+// fragments already in registers), each closed by a workgroup barrier.  Group 1 starts one
+// barrier late, so at any time one group computes while the other moves data, and each
+// SIMD's matrix core is fed by whichever of its two waves is in its compute phase.
+//
+// Row interleave: MFMA tile i of group p holds tile rows 128p + 4t + i (t = 0..31, the MFMA
+// row) and MFMA tile j of wave i holds columns 64i + 2t + j.  The DMA places those rows at
+// LDS rows 128p + 32i + t (resp. 64i + 32j + t), so fragment reads and the bank-conflict-free
+// swizzle are unchanged, while a lane's four A scales (rows 4t..4t+3) and two B scales
+// (columns 2t, 2t+1) are adjacent bytes: one LDS read each, the byte picked by the MFMA's
+// scale selector.  In the epilogue a lane then holds 2 adjacent columns of 4 adjacent rows,
+// and writes column pairs.
+//
+// Stage k+3 is issued in M_k into the buffer stage k-1 used; both groups have read stage k-1
+// before the barrier that closes slot 2k-1, and M_k of either group lies after it.  M_k ends
+// by waiting for this wave's part of stage k+1; the barrier closing slot 2k+1 publishes the
+// whole stage before group 0 reads it in M_{k+1}.
+
+constexpr int PP_NST = 4;
+
+// LDS reads the compiler does not track (the 32 low bits of a generic LDS address are its
+// LDS offset); the caller waits for them with lgkmcnt
+__device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* p) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_read_b32(const uint8_t* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* p) {
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return v;
+}
+// buffer resource word 3 for raw byte-addressed buffers on gfx9 (32-bit data format, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+
+template <int MODE, int FA, int FB, int OUT>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                         const void* __restrict__ sa_p, const void* __restrict__ sb_p,
+                                                         void* __restrict__ C, int M, int N, int K, int tiles_m,
+                                                         int tiles_n) {
+  constexpr bool MX = MODE == MODE_MX;
+  // MX: each group loads its own copy of the stage's scale rows, so that every wave issues the
+  // same loads and the steady-state loop has no group-dependent branch
+  constexpr int STAGE = BIG_TILE_BYTES + (MX ? 2 * BIG_SCALE_BYTES : 0);
+  static_assert(PP_NST == 4, "the main loop is unrolled for 4 stages");
+  // one LDS array per stage: distinct objects let the compiler see that a DMA into one stage
+  // does not alias fragment reads from another
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wi = wave & 3;
+  const int g = lane >> 5, r = lane & 31;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
+  const int nk = K / BIG_BK;
+
+  // ---- this group's half of each stage: group 0 the A rows, group 1 the B rows, through a
+  //      buffer resource (uniform base, 32-bit lane offsets, range = the rows present); rows
+  //      past the matrix edge re-read its last row
+  const int lim = grp == 0 ? M - m0 : N - n0;
+  const uint8_t* d_base = grp == 0 ? A + (size_t)m0 * K : B + (size_t)n0 * K;
+  const uint64_t d_bytes = (uint64_t)lim * (uint64_t)K;
+  const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(d_base), (short)0, (int)(d_bytes < 0xFFFFFFFFull ? d_bytes : 0xFFFFFFFFull), kBufferFlags);
+  const int d_lds = grp * (BIG_BM * BIG_BK);
+  uint32_t od[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (wi * 4 + i) * 64 + lane;
+    const int q = slot >> 2, c = (slot & 3) ^ bswz_pos(q);  // LDS row q, global 16-byte chunk c
+    const int row = grp == 0 ? (q & ~127) + 4 * (q & 31) + ((q >> 5) & 3)   // A: 128p + 4t + i
+                             : (q & ~63) + 2 * (q & 31) + ((q >> 5) & 1);   // B: 64w + 2t + j
+    const int rr = row < lim ? row : lim - 1;
+    od[i] = (uint32_t)rr * (uint32_t)K + c * 16;
+  }
+  // MX scales: wave i of each group loads scale row i of the stage (A K-blocks 2s, 2s+1, then
+  // B's) into its group's copy
+  __amdgpu_buffer_rsrc_t s_rsrc = d_rsrc;  // replaced below (MX)
+  uint32_t os = 0;
+  int s_lim = 0;
+  if constexpr (MX) {
+    const bool isb = wi >= 2;
+    s_lim = isb ? N : M;
+    const int base_row = isb ? n0 : m0;
+    const uint8_t* s_base = static_cast<const uint8_t*>(isb ? sb_p : sa_p) + (size_t)(wi & 1) * s_lim + base_row;
+    const uint64_t s_bytes = (uint64_t)(K / 32) * s_lim - ((uint64_t)(wi & 1) * s_lim + base_row);
+    s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(s_base), (short)0,
+                                               (int)(s_bytes < 0xFFFFFFFFull ? s_bytes : 0xFFFFFFFFull), kBufferFlags);
+    const int rel = lane * 4, room = s_lim - 4 - base_row;  // M, N multiples of 4 here
+    os = (uint32_t)(rel < room ? rel : room);
+  }
+  auto issue = [&](int ks, uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rsrc, (lds_ptr_t)(buf + d_lds + (wi * 4 + i) * 1024), 16, od[i],
+                                               ks * BIG_BK, 0, 0);
+    if constexpr (MX)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          s_rsrc, (lds_ptr_t)(buf + BIG_TILE_BYTES + grp * BIG_SCALE_BYTES + wi * 256), 4, os, 2 * ks * s_lim, 0, 0);
+  };
+  // wait until at most `later` stages of this wave's loads are in flight (they retire in order)
+  auto wait_stage = [&](int later) {
+    if (later >= 2) {
+      if constexpr (MX) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else if (later == 1) {
+      if constexpr (MX) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // fragments of one stage; sa / sb pack the e8m0 bytes of tiles i = 0..3 / j = 0..1.  The
+  // LDS reads are issued as inline assembly: the compiler cannot tell that they never touch a
+  // stage with loads still in flight and would otherwise wait for every outstanding load
+  // (each read's stage was published by an explicit vmcnt wait and barrier, and the reads are
+  // waited for explicitly with lgkmcnt(0)).
+  v8i fa[4], fb[2];
+  int fsa = 0, fsb = 0;
+  auto frag = [&](const uint8_t* base, int row) -> v8i {
+    const u32x4 lo = lds_read_b128(base + bswz(row, g));
+    const u32x4 hi = lds_read_b128(base + bswz(row, g + 2));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto read_frags = [&](const uint8_t* buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = frag(buf + BIG_BM * BIG_BK, wi * 64 + 32 * j + r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(buf, grp * 128 + 32 * i + r);
+    if constexpr (MX) {
+      const uint8_t* sbase = buf + BIG_TILE_BYTES + grp * BIG_SCALE_BYTES;
+      fsa = (int)lds_read_b32(sbase + g * 256 + grp * 128 + 4 * r);
+      fsb = (int)lds_read_u16(sbase + 512 + g * 256 + wi * 64 + 2 * r);
+    }
+  };
+#define SFP8_PP_MFMA(I, J)                                                                                    \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[J], acc[I][J], FA, FB, MX ? I : 0, fsa, \
+                                                               MX ? J : 0, fsb)
+  auto compute = [&]() {
+    SFP8_PP_MFMA(0, 0);
+    SFP8_PP_MFMA(0, 1);
+    SFP8_PP_MFMA(1, 0);
+    SFP8_PP_MFMA(1, 1);
+    SFP8_PP_MFMA(2, 0);
+    SFP8_PP_MFMA(2, 1);
+    SFP8_PP_MFMA(3, 0);
+    SFP8_PP_MFMA(3, 1);
+  };
+#undef SFP8_PP_MFMA
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // M_k then C_k.  The barrier closing slot 2nk-1 (group 0 after C_{nk-1}, group 1 after
+  // M_{nk-1}) and group 1's last one are dropped: no LDS is written or read after them.
+  // STEADY steps (stage k+3 exists) contain no branch, so the compiler keeps each phase's
+  // MFMAs between its two barriers instead of sinking them into later blocks.
+  auto step = [&](auto steady, int k, const uint8_t* cur, uint8_t* refill) {
+    constexpr bool STEADY = decltype(steady)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    if (STEADY || k + 3 < nk) issue(k + 3, refill);
+    read_frags(cur);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments in registers
+    if constexpr (STEADY) {
+      wait_stage(2);
+      barrier();
+    } else {
+      if (k + 1 < nk) wait_stage(nk - k - 2 < 2 ? nk - k - 2 : 2);
+      if (!(grp == 1 && k + 1 == nk)) barrier();
+    }
+    compute();
+    if (STEADY || k + 1 < nk) barrier();
+  };
+  using steady_t = std::integral_constant<bool, true>;
+  using tail_t = std::integral_constant<bool, false>;
+
+  if (nk > 0) {
+    issue(0, lds0);
+    if (nk > 1) issue(1, lds1);
+    if (nk > 2) issue(2, lds2);
+    wait_stage(nk - 1 < 2 ? nk - 1 : 2);  // this wave's part of stage 0 landed
+    barrier();                            // stage 0 visible
+    if (grp == 1) barrier();              // group 1 sits out slot 0
+    int k = 0;
+    for (; k + 7 <= nk; k += 4) {  // stages k .. k+3 each have a stage 3 ahead to issue
+      step(steady_t{}, k, lds0, lds3);
+      step(steady_t{}, k + 1, lds1, lds0);
+      step(steady_t{}, k + 2, lds2, lds1);
+      step(steady_t{}, k + 3, lds3, lds2);
+    }
+    for (; k < nk; k += 4) {
+      step(tail_t{}, k, lds0, lds3);
+      if (k + 1 < nk) step(tail_t{}, k + 1, lds1, lds0);
+      if (k + 2 < nk) step(tail_t{}, k + 2, lds2, lds1);
+      if (k + 3 < nk) step(tail_t{}, k + 3, lds3, lds2);
+    }
+  }
+
+  // ---- epilogue: result register e of tile (i, j) is tile row 128p + 4(8(e/4) + 4g + e%4) + i,
+  //      column 64w + 2r + j: each lane writes column pairs (2r, 2r+1)
+  float scale = 1.0f;
+  if constexpr (MODE == MODE_TENSOR) scale = *static_cast<const float*>(sa_p) * *static_cast<const float*>(sb_p);
+  const int gn = n0 + wi * 64 + 2 * r;
+  const bool pair = (N & 1) == 0 && gn + 1 < N;  // both columns present, pair store aligned
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gm = m0 + grp * 128 + 4 * (8 * (e >> 2) + 4 * g + (e & 3)) + i;
+      if (gm >= M) continue;
+      float v0 = acc[i][0][e], v1 = acc[i][1][e];
+      if constexpr (MODE == MODE_TENSOR) {
+        v0 *= scale;
+        v1 *= scale;
+      }
+      const size_t at = (size_t)gm * N + gn;
+      if constexpr (OUT == OUT_F32) {
+        float* c = static_cast<float*>(C) + at;
+        if (pair) {
+          *reinterpret_cast<float2*>(c) = make_float2(v0, v1);
+        } else {
+          if (gn < N) c[0] = v0;
+          if (gn + 1 < N) c[1] = v1;
+        }
+      } else {
+        uint16_t* c = static_cast<uint16_t*>(C) + at;
+        const uint32_t b0 = f32_to_bf16_bits(v0), b1 = f32_to_bf16_bits(v1);
+        if (pair) {
+          *reinterpret_cast<uint32_t*>(c) = b0 | (b1 << 16);
+        } else {
+          if (gn < N) c[0] = (uint16_t)b0;
+          if (gn + 1 < N) c[1] = (uint16_t)b1;
+        }
+      }
+    }
+}
+
+constexpr bool kUsePingPong = true;
+
 template <int MODE, int FA, int FB, int OUT>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, void* C, int M, int N, int K,
                        hipStream_t st) {
@@ -503,8 +770,15 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
     // large problems only (>= half a wave of tiles on 256 CUs); MX scale rows are read as
     // 4-byte runs, so M and N must be multiples of 4 there
     if (tiles_m * tiles_n >= 128 && M >= 4 && N >= 4 && (MODE != MODE_MX || (M % 4 == 0 && N % 4 == 0))) {
-      hipLaunchKernelGGL((gemm_big_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(256), 0, st, A, B, sa, sb,
-                         C, M, N, K, tiles_m, tiles_n);
+      // the ping-pong kernel addresses a tile's rows and a stage's scale rows with 32-bit offsets
+      const int64_t mn = M > N ? M : N;
+      const bool offsets32 = 256ll * K < (1ll << 32) && (MODE != MODE_MX || (int64_t)(K / 32) * mn < (1ll << 32));
+      if (kUsePingPong && offsets32)
+        hipLaunchKernelGGL((gemm_pp_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B, sa,
+                           sb, C, M, N, K, tiles_m, tiles_n);
+      else
+        hipLaunchKernelGGL((gemm_big_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(256), 0, st, A, B, sa,
+                           sb, C, M, N, K, tiles_m, tiles_n);
       return check_launch("fp8_gemm");
     }
   }
