@@ -502,46 +502,58 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
 // of a group computes tile columns 64i .. 64i+63 (a 128 x 64 wave tile: 4 x 2 MFMAs of
 // 32x32x64 per K step, 128 fp32 accumulators per lane).  Waves w and w+4 share a SIMD.
 //
-// Every wave runs the same sequence M_0 C_0 M_1 C_1 ... of memory phases (issue this wave's
-// part of stage k+3, read stage k's fragments from LDS) and compute phases (8 MFMAs on
-// fragments already in registers), each closed by a workgroup barrier.  Group 1 starts one
-// barrier late, so at any time one group computes while the other moves data, and each
-// SIMD's matrix core is fed by whichever of its two waves is in its compute phase.
+// Every wave runs the same sequence M_0 C_0 M_1 C_1 ..., each phase closed by a workgroup
+// barrier; group 1 starts one barrier late, so at any time one group computes while the
+// other moves data, and each SIMD's matrix core is fed by whichever of its two waves is in
+// its compute phase.
+//   M_k: issue this wave's part of stage k+3 into the buffer stage k-1 used; read stage k's
+//        A fragments (and A scales).
+//   C_k: the 8 MFMAs of stage k; meanwhile read stage k+1's B fragments (and B scales) into
+//        the other B register set, so that both waves of a SIMD keep LDS reads in flight;
+//        then wait for this wave's part of stage k+2.
+// Slot 2k holds M_k of group 0 and C_{k-1} of group 1; slot 2k+1 holds C_k of group 0 and
+// M_k of group 1.  Stage k+2 is complete (both groups waited for it by the ends of slots
+// 2k+1 and 2k+2) and published by the barrier closing slot 2k+2, before group 0 reads its B
+// fragments in slot 2k+3.  Stage k-1's buffer is last read in slot 2k-1 (group 1's M_{k-1}),
+// and every read is waited for (lgkmcnt) before the barrier that closes the reading wave's
+// next memory phase, so the refill issued from slot 2k on overwrites nothing still needed.
 //
 // Row interleave: MFMA tile i of group p holds tile rows 128p + 4t + i (t = 0..31, the MFMA
 // row) and MFMA tile j of wave i holds columns 64i + 2t + j.  The DMA places those rows at
-// LDS rows 128p + 32i + t (resp. 64i + 32j + t), so fragment reads and the bank-conflict-free
-// swizzle are unchanged, while a lane's four A scales (rows 4t..4t+3) and two B scales
-// (columns 2t, 2t+1) are adjacent bytes: one LDS read each, the byte picked by the MFMA's
-// scale selector.  In the epilogue a lane then holds 2 adjacent columns of 4 adjacent rows,
-// and writes column pairs.
+// LDS rows 128p + 32i + t (resp. 64i + 32j + t), so fragment reads keep the bank-conflict-free
+// swizzle, while a lane's four A scales (rows 4t..4t+3) and two B scales (columns 2t, 2t+1)
+// are adjacent bytes: one LDS read each, the byte picked by the MFMA's scale selector.  In
+// the epilogue a lane then holds 2 adjacent columns of 4 adjacent rows, and writes pairs.
 //
-// Stage k+3 is issued in M_k into the buffer stage k-1 used; both groups have read stage k-1
-// before the barrier that closes slot 2k-1, and M_k of either group lies after it.  M_k ends
-// by waiting for this wave's part of stage k+1; the barrier closing slot 2k+1 publishes the
-// whole stage before group 0 reads it in M_{k+1}.
+// LDS reads are inline assembly with immediate offsets from a few per-lane base registers:
+// the compiler neither tracks them (it cannot tell that they never touch a stage with loads
+// in flight, and would wait for every outstanding load) nor needs registers per address.
 
 constexpr int PP_NST = 4;
-
-// LDS reads the compiler does not track (the 32 low bits of a generic LDS address are its
-// LDS offset); the caller waits for them with lgkmcnt
-__device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* p) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
-  return v;
-}
-__device__ __forceinline__ uint32_t lds_read_b32(const uint8_t* p) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
-  return v;
-}
-__device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* p) {
-  uint32_t v;
-  asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
-  return v;
-}
 // buffer resource word 3 for raw byte-addressed buffers on gfx9 (32-bit data format, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
+
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16(uint32_t vaddr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field is 16 bits");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(vaddr), "i"(OFF) : "memory");
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t ds_read4(uint32_t vaddr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field is 16 bits");
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(vaddr), "i"(OFF) : "memory");
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t ds_read2(uint32_t vaddr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field is 16 bits");
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1 offset:%2" : "=v"(v) : "v"(vaddr), "i"(OFF) : "memory");
+  return v;
+}
 
 template <int MODE, int FA, int FB, int OUT>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
@@ -552,13 +564,10 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   // MX: each group loads its own copy of the stage's scale rows, so that every wave issues the
   // same loads and the steady-state loop has no group-dependent branch
   constexpr int STAGE = BIG_TILE_BYTES + (MX ? 2 * BIG_SCALE_BYTES : 0);
+  constexpr int B_OFF = BIG_BM * BIG_BK, S_OFF = BIG_TILE_BYTES;
   static_assert(PP_NST == 4, "the main loop is unrolled for 4 stages");
-  // one LDS array per stage: distinct objects let the compiler see that a DMA into one stage
-  // does not alias fragment reads from another
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[STAGE];
+  static_assert(STAGE + B_OFF + 2048 + 16 < 65536, "stage 1 offsets must fit the LDS offset field");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PP_NST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -577,7 +586,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   const uint64_t d_bytes = (uint64_t)lim * (uint64_t)K;
   const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(d_base), (short)0, (int)(d_bytes < 0xFFFFFFFFull ? d_bytes : 0xFFFFFFFFull), kBufferFlags);
-  const int d_lds = grp * (BIG_BM * BIG_BK);
+  const int d_lds = grp * B_OFF;
   uint32_t od[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -604,14 +613,15 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     const int rel = lane * 4, room = s_lim - 4 - base_row;  // M, N multiples of 4 here
     os = (uint32_t)(rel < room ? rel : room);
   }
-  auto issue = [&](int ks, uint8_t* buf) {
+  auto issue = [&](int ks, int st) {
+    uint8_t* buf = smem + st * STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rsrc, (lds_ptr_t)(buf + d_lds + (wi * 4 + i) * 1024), 16, od[i],
                                                ks * BIG_BK, 0, 0);
     if constexpr (MX)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          s_rsrc, (lds_ptr_t)(buf + BIG_TILE_BYTES + grp * BIG_SCALE_BYTES + wi * 256), 4, os, 2 * ks * s_lim, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(buf + S_OFF + grp * BIG_SCALE_BYTES + wi * 256), 4,
+                                               os, 2 * ks * s_lim, 0, 0);
   };
   // wait until at most `later` stages of this wave's loads are in flight (they retire in order)
   auto wait_stage = [&](int later) {
@@ -626,6 +636,22 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     }
   };
 
+  // ---- per-lane LDS base addresses; stage s, tile i adds the immediate s*STAGE + i*2048
+  //      (stages 2 and 3 from a second set of bases, to keep offsets within 16 bits)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t row_lo = r * 64 + ((g ^ bswz_pos(r)) << 4), row_hi = r * 64 + (((g + 2) ^ bswz_pos(r)) << 4);
+  uint32_t a_lo[2], a_hi[2], b_lo[2], b_hi[2], s_a[2], s_b[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t base = lds0 + h * 2 * STAGE;
+    a_lo[h] = base + grp * 128 * 64 + row_lo;
+    a_hi[h] = base + grp * 128 * 64 + row_hi;
+    b_lo[h] = base + B_OFF + wi * 64 * 64 + row_lo;
+    b_hi[h] = base + B_OFF + wi * 64 * 64 + row_hi;
+    s_a[h] = base + S_OFF + grp * BIG_SCALE_BYTES + g * 256 + grp * 128 + 4 * r;
+    s_b[h] = base + S_OFF + grp * BIG_SCALE_BYTES + 512 + g * 256 + wi * 64 + 2 * r;
+  }
+
   v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -634,33 +660,34 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragments of one stage; sa / sb pack the e8m0 bytes of tiles i = 0..3 / j = 0..1.  The
-  // LDS reads are issued as inline assembly: the compiler cannot tell that they never touch a
-  // stage with loads still in flight and would otherwise wait for every outstanding load
-  // (each read's stage was published by an explicit vmcnt wait and barrier, and the reads are
-  // waited for explicitly with lgkmcnt(0)).
-  v8i fa[4], fb[2];
-  int fsa = 0, fsb = 0;
-  auto frag = [&](const uint8_t* base, int row) -> v8i {
-    const u32x4 lo = lds_read_b128(base + bswz(row, g));
-    const u32x4 hi = lds_read_b128(base + bswz(row, g + 2));
+  // fragments: A of the current stage, B of the current and the next stage (two sets);
+  // fsa / fsb pack the e8m0 bytes of tiles i = 0..3 / j = 0..1
+  v8i fa[4], fb[2][2];
+  int fsa = 0, fsb[2] = {0, 0};
+  auto pack = [](const u32x4& lo, const u32x4& hi) -> v8i {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  auto read_frags = [&](const uint8_t* buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = frag(buf + BIG_BM * BIG_BK, wi * 64 + 32 * j + r);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = frag(buf, grp * 128 + 32 * i + r);
-    if constexpr (MX) {
-      const uint8_t* sbase = buf + BIG_TILE_BYTES + grp * BIG_SCALE_BYTES;
-      fsa = (int)lds_read_b32(sbase + g * 256 + grp * 128 + 4 * r);
-      fsb = (int)lds_read_u16(sbase + 512 + g * 256 + wi * 64 + 2 * r);
-    }
+  // ST: stage buffer 0..3 (compile time); SET: B register set
+  auto read_a = [&](auto st_c) {
+    constexpr int ST = decltype(st_c)::value, H = ST >> 1, O = (ST & 1) * STAGE;
+    fa[0] = pack(ds_read16<O + 0 * 2048>(a_lo[H]), ds_read16<O + 0 * 2048>(a_hi[H]));
+    fa[1] = pack(ds_read16<O + 1 * 2048>(a_lo[H]), ds_read16<O + 1 * 2048>(a_hi[H]));
+    fa[2] = pack(ds_read16<O + 2 * 2048>(a_lo[H]), ds_read16<O + 2 * 2048>(a_hi[H]));
+    fa[3] = pack(ds_read16<O + 3 * 2048>(a_lo[H]), ds_read16<O + 3 * 2048>(a_hi[H]));
+    if constexpr (MX) fsa = (int)ds_read4<O>(s_a[H]);
   };
-#define SFP8_PP_MFMA(I, J)                                                                                    \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[J], acc[I][J], FA, FB, MX ? I : 0, fsa, \
-                                                               MX ? J : 0, fsb)
-  auto compute = [&]() {
+  auto read_b = [&](auto st_c, auto set_c) {
+    constexpr int ST = decltype(st_c)::value, H = ST >> 1, O = (ST & 1) * STAGE;
+    constexpr int SET = decltype(set_c)::value;
+    fb[SET][0] = pack(ds_read16<O + 0 * 2048>(b_lo[H]), ds_read16<O + 0 * 2048>(b_hi[H]));
+    fb[SET][1] = pack(ds_read16<O + 1 * 2048>(b_lo[H]), ds_read16<O + 1 * 2048>(b_hi[H]));
+    if constexpr (MX) fsb[SET] = (int)ds_read2<O>(s_b[H]);
+  };
+#define SFP8_PP_MFMA(I, J)                                                                                     \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[SET][J], acc[I][J], FA, FB, MX ? I : 0, \
+                                                               fsa, MX ? J : 0, fsb[SET])
+  auto compute = [&](auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
     SFP8_PP_MFMA(0, 0);
     SFP8_PP_MFMA(0, 1);
     SFP8_PP_MFMA(1, 0);
@@ -676,48 +703,61 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // M_k then C_k.  The barrier closing slot 2nk-1 (group 0 after C_{nk-1}, group 1 after
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // M_k then C_k for stage k in buffer ST (= k % 4), B set SET (= k % 2).  STEADY steps (stage
+  // k+3 exists) contain no branch, so the compiler keeps each phase's MFMAs between its two
+  // barriers.  The barrier closing slot 2nk-1 (group 0 after C_{nk-1}, group 1 after
   // M_{nk-1}) and group 1's last one are dropped: no LDS is written or read after them.
-  // STEADY steps (stage k+3 exists) contain no branch, so the compiler keeps each phase's
-  // MFMAs between its two barriers instead of sinking them into later blocks.
-  auto step = [&](auto steady, int k, const uint8_t* cur, uint8_t* refill) {
+  auto step = [&](auto steady, auto st_c, auto set_c, int k) {
     constexpr bool STEADY = decltype(steady)::value;
+    constexpr int ST = decltype(st_c)::value, SET = decltype(set_c)::value;
+    using NextSt = std::integral_constant<int, (ST + 1) & 3>;
+    using NextSet = std::integral_constant<int, SET ^ 1>;
     __builtin_amdgcn_sched_barrier(0);
-    if (STEADY || k + 3 < nk) issue(k + 3, refill);
-    read_frags(cur);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments in registers
+    if (STEADY || k + 3 < nk) issue(k + 3, (ST + 3) & 3);
+    read_a(st_c);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // A (and the previous C's B) in registers
+    if (STEADY || !(grp == 1 && k + 1 == nk)) barrier();
+    // next B set first: the reads are asynchronous, and issuing them while the current
+    // fragments are still live keeps their destinations off the registers the MFMAs read
+    if (STEADY || k + 1 < nk) read_b(NextSt{}, NextSet{});
+    __builtin_amdgcn_sched_barrier(0);
+    compute(set_c);
+    __builtin_amdgcn_sched_barrier(0);  // the wait below must not split the MFMA run
     if constexpr (STEADY) {
-      wait_stage(2);
-      barrier();
+      wait_stage(1);  // this wave's part of stage k+2
     } else {
-      if (k + 1 < nk) wait_stage(nk - k - 2 < 2 ? nk - k - 2 : 2);
-      if (!(grp == 1 && k + 1 == nk)) barrier();
+      if (k + 2 < nk) wait_stage(nk - k - 3 < 1 ? nk - k - 3 : 1);
     }
-    compute();
     if (STEADY || k + 1 < nk) barrier();
   };
   using steady_t = std::integral_constant<bool, true>;
   using tail_t = std::integral_constant<bool, false>;
 
   if (nk > 0) {
-    issue(0, lds0);
-    if (nk > 1) issue(1, lds1);
-    if (nk > 2) issue(2, lds2);
-    wait_stage(nk - 1 < 2 ? nk - 1 : 2);  // this wave's part of stage 0 landed
-    barrier();                            // stage 0 visible
-    if (grp == 1) barrier();              // group 1 sits out slot 0
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    if (nk > 2) issue(2, 2);
+    wait_stage(nk - 2 < 1 ? (nk - 2 < 0 ? 0 : nk - 2) : 1);  // this wave's parts of stages 0 and 1
+    barrier();                                               // stages 0 and 1 visible
+    read_b(I0{}, I0{});                                      // stage 0's B set
+    if (grp == 1) barrier();                                 // group 1 sits out slot 0
     int k = 0;
     for (; k + 7 <= nk; k += 4) {  // stages k .. k+3 each have a stage 3 ahead to issue
-      step(steady_t{}, k, lds0, lds3);
-      step(steady_t{}, k + 1, lds1, lds0);
-      step(steady_t{}, k + 2, lds2, lds1);
-      step(steady_t{}, k + 3, lds3, lds2);
+      step(steady_t{}, I0{}, I0{}, k);
+      step(steady_t{}, I1{}, I1{}, k + 1);
+      step(steady_t{}, I2{}, I0{}, k + 2);
+      step(steady_t{}, I3{}, I1{}, k + 3);
     }
     for (; k < nk; k += 4) {
-      step(tail_t{}, k, lds0, lds3);
-      if (k + 1 < nk) step(tail_t{}, k + 1, lds1, lds0);
-      if (k + 2 < nk) step(tail_t{}, k + 2, lds2, lds1);
-      if (k + 3 < nk) step(tail_t{}, k + 3, lds3, lds2);
+      step(tail_t{}, I0{}, I0{}, k);
+      if (k + 1 < nk) step(tail_t{}, I1{}, I1{}, k + 1);
+      if (k + 2 < nk) step(tail_t{}, I2{}, I0{}, k + 2);
+      if (k + 3 < nk) step(tail_t{}, I3{}, I1{}, k + 3);
     }
   }
 
