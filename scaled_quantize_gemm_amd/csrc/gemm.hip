@@ -530,6 +530,10 @@ __global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restr
 // in flight, and would wait for every outstanding load) nor needs registers per address.
 
 constexpr int PP_NST = 4;
+// MFMAs of a compute phase issued before its loads of the next B fragments
+constexpr int kPPLead = 2;
+// memory phase: fragment reads before the stage refill's loads
+constexpr bool kPPReadsFirst = true;
 // buffer resource word 3 for raw byte-addressed buffers on gfx9 (32-bit data format, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
@@ -683,21 +687,38 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     fb[SET][1] = pack(ds_read16<O + 1 * 2048>(b_lo[H]), ds_read16<O + 1 * 2048>(b_hi[H]));
     if constexpr (MX) fsb[SET] = (int)ds_read2<O>(s_b[H]);
   };
-#define SFP8_PP_MFMA(I, J)                                                                                     \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[SET][J], acc[I][J], FA, FB, MX ? I : 0, \
-                                                               fsa, MX ? J : 0, fsb[SET])
-  auto compute = [&](auto set_c) {
-    constexpr int SET = decltype(set_c)::value;
-    SFP8_PP_MFMA(0, 0);
-    SFP8_PP_MFMA(0, 1);
-    SFP8_PP_MFMA(1, 0);
-    SFP8_PP_MFMA(1, 1);
-    SFP8_PP_MFMA(2, 0);
-    SFP8_PP_MFMA(2, 1);
-    SFP8_PP_MFMA(3, 0);
-    SFP8_PP_MFMA(3, 1);
+  // MFMA n of a stage: tile (n / 2, n % 2)
+  auto mfma = [&](auto n_c, auto set_c) {
+    constexpr int n = decltype(n_c)::value, I = n / 2, J = n % 2, SET = decltype(set_c)::value;
+    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[I], fb[SET][J], acc[I][J], FA, FB, MX ? I : 0, fsa,
+                                                                 MX ? J : 0, fsb[SET]);
   };
-#undef SFP8_PP_MFMA
+  // the stage's 8 MFMAs with `between` issued after the first kPPLead of them; the fragments
+  // stay live to the end, so that loads issued in `between` never target registers an
+  // earlier MFMA of this run reads
+  auto compute = [&](auto set_c, auto&& between) {
+    constexpr int SET = decltype(set_c)::value;
+    auto at = [&](auto n_c) {
+      constexpr int n = decltype(n_c)::value;
+      if constexpr (n == kPPLead) {
+        __builtin_amdgcn_sched_barrier(0);
+        between();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma(n_c, set_c);
+    };
+    at(std::integral_constant<int, 0>{});
+    at(std::integral_constant<int, 1>{});
+    at(std::integral_constant<int, 2>{});
+    at(std::integral_constant<int, 3>{});
+    at(std::integral_constant<int, 4>{});
+    at(std::integral_constant<int, 5>{});
+    at(std::integral_constant<int, 6>{});
+    at(std::integral_constant<int, 7>{});
+    __builtin_amdgcn_sched_barrier(0);
+    const v8i a0 = fa[0], a1 = fa[1], a2 = fa[2], a3 = fa[3], b0 = fb[SET][0], b1 = fb[SET][1];
+    asm volatile("" ::"v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1));
+  };
   auto barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_barrier" ::: "memory");
@@ -718,15 +739,20 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     using NextSt = std::integral_constant<int, (ST + 1) & 3>;
     using NextSet = std::integral_constant<int, SET ^ 1>;
     __builtin_amdgcn_sched_barrier(0);
-    if (STEADY || k + 3 < nk) issue(k + 3, (ST + 3) & 3);
-    read_a(st_c);
+    if constexpr (kPPReadsFirst) {
+      read_a(st_c);
+      __builtin_amdgcn_sched_barrier(0);
+      if (STEADY || k + 3 < nk) issue(k + 3, (ST + 3) & 3);
+    } else {
+      if (STEADY || k + 3 < nk) issue(k + 3, (ST + 3) & 3);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(st_c);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // A (and the previous C's B) in registers
     if (STEADY || !(grp == 1 && k + 1 == nk)) barrier();
-    // next B set first: the reads are asynchronous, and issuing them while the current
-    // fragments are still live keeps their destinations off the registers the MFMAs read
-    if (STEADY || k + 1 < nk) read_b(NextSt{}, NextSet{});
-    __builtin_amdgcn_sched_barrier(0);
-    compute(set_c);
+    compute(set_c, [&]() {
+      if (STEADY || k + 1 < nk) read_b(NextSt{}, NextSet{});
+    });
     __builtin_amdgcn_sched_barrier(0);  // the wait below must not split the MFMA run
     if constexpr (STEADY) {
       wait_stage(1);  // this wave's part of stage k+2
