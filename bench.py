@@ -15,7 +15,8 @@ One step = the whole path once over that batch, inputs resident in HBM:
 Printed: one JSON line.  value = the step's GEMM FLOPs / step time (TFLOP/s, the whole
 step, casts included); per-kernel figures from HIP events on the launch stream over the
 timed region; roofline of the dominant kernel (the GEMM, against dense FP8 MFMA peak)
-and of the amax + cast stream (against HBM peak); the CPU oracle timed on a bounded sample.
+and of the standalone amax + cast stream (against HBM peak, timed over back-to-back
+launches after the steps); the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
@@ -92,7 +93,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device-to-device copy of known size (counter calibration)")
@@ -175,11 +176,24 @@ def main():
     per = {n: sum(events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)) / args.steps
            for i, n in enumerate(names)}
 
+    # the standalone amax + cast of the 2^28-element tensor, back to back on its own: its HBM
+    # roofline (inside the step it also absorbs the write-back of the GEMM's output)
+    standalone = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(standalone):
+        sq.fp8_quantize(T, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=scale, amax_slot=amax_slot, q=qt)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_alone_ms = e0.elapsed_time(e1) / standalone
+
     gemm_flops = 2.0 * M * N * K
     stream_bytes = NUMEL * (2 + 1)  # bf16 read + E4M3 write (amax is a scalar)
     mxq_bytes = M * K * (2 + 1) + M * (K // 32)
     gemm_tflops = gemm_flops / (per["gemm_mx"] * 1e-3) / 1e12
-    stream_gbs = stream_bytes / (per["amax_cast_stream"] * 1e-3) / 1e9
+    stream_gbs = stream_bytes / (stream_alone_ms * 1e-3) / 1e9
+    stream_step_gbs = stream_bytes / (per["amax_cast_stream"] * 1e-3) / 1e9
     mxq_gbs = mxq_bytes / (per["mx_quantize_A"] * 1e-3) / 1e9
     value = gemm_flops / (ms_step * 1e-3) / 1e12
 
@@ -204,7 +218,9 @@ def main():
                      "traffic": _traffic("gemm_mx", ["gemm.hip", "common.h"])},
         "roofline_amax_cast": {"kernel": "amax_cast_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
-                               "traffic": _traffic("amax_cast_stream", ["quantize.hip", "common.h"])},
+                               "traffic": _traffic("amax_cast_stream", ["quantize.hip", "common.h"]),
+                               "timing": f"{standalone} back-to-back launches after the timed steps",
+                               "in_step_gbs": round(stream_step_gbs, 1)},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in per.items()},
         "mx_quantize_gbs": round(mxq_gbs, 1),
     }

@@ -207,12 +207,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
 
 // ------------------------------------------------------------------ large-tile kernel
 //
-// 256 x 256 block tile for large problems (per-tensor and MX scaling).  K is staged 64 at a
-// time through NST LDS stages, each filled by direct global -> LDS loads
-// (global_load_lds_dwordx4: lane L's 16 bytes land at the wave's LDS base + 16 L) issued
-// NST-1 stages ahead, so no registers hold tiles in flight.  4 waves in a 2 x 2 grid, each a
-// 128 x 128 wave tile of 4 x 4 v_mfma_*_32x32x64_f8f6f4 (16 fp32 accumulators per tile and
-// lane).  Fragments for stage s+1 are read from LDS while the MFMAs of stage s run.
+// Definitions shared by the large-tile kernel below: a 256 x 256 block tile for large
+// problems (per-tensor and MX scaling), K staged 64 at a time through LDS stages that are
+// filled by direct-to-LDS loads (lane L's 16 bytes land at the instruction's LDS base + 16 L),
+// so no registers hold tiles in flight.
 //
 // 32x32x64 operand layout: lane l = 32 g + r supplies row r; bytes 0-15 hold K = 16g..16g+15
 // and bytes 16-31 K = 32+16g..; result register e of lane l is C[8(e/4) + 4g + e%4][r]; in the
@@ -232,7 +230,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int BIG_BM = 256, BIG_BN = 256, BIG_BK = 64;
 constexpr int BIG_TILE_BYTES = (BIG_BM + BIG_BN) * BIG_BK;  // 32 KB
 constexpr int BIG_SCALE_BYTES = 2 * (BIG_BM + BIG_BN);      // 1 KB (MX only)
-constexpr int BIG_NST = 4;
 
 __device__ __forceinline__ int bswz_pos(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }
 __device__ __forceinline__ int bswz(int row, int c) { return row * 64 + ((c ^ bswz_pos(row)) << 4); }
@@ -253,252 +250,10 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Workgroup barrier for the DMA pipeline: this wave's LDS reads are complete (lgkmcnt(0)) and
-// every wave has arrived.  The caller has already waited (vmcnt) for exactly the stage it is
-// about to read; a __syncthreads() fence would also drain every later prefetch in flight.
-// The "memory" clobber keeps the compiler from moving LDS accesses across it.
-// The lgkmcnt(0) wait is the builtin (encoding: vmcnt 63, expcnt 7, lgkmcnt 0) so that the
-// compiler's wait-count tracking knows every LDS read has completed at this point.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("s_barrier" ::: "memory");
-}
-
-template <int MODE, int FA, int FB, int OUT>
-__global__ void __launch_bounds__(256, 1) gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-                                                          const void* __restrict__ sa_p, const void* __restrict__ sb_p,
-                                                          void* __restrict__ C, int M, int N, int K, int tiles_m,
-                                                          int tiles_n) {
-  constexpr int NST = BIG_NST;
-  constexpr bool MX = MODE == MODE_MX;
-  constexpr int STAGE = BIG_TILE_BYTES + (MX ? BIG_SCALE_BYTES : 0);
-  // one LDS array per stage: distinct objects let the compiler see that a DMA into one stage
-  // does not alias fragment reads from another
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[STAGE];
-  static_assert(NST == 4, "the main loop is unrolled for 4 stages");
-  auto stage_buf = [&](int st) -> uint8_t* { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;
-  const int g = lane >> 5, r = lane & 31;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
-  const int nk = K / BIG_BK;
-
-  // ---- direct-to-LDS loads: uniform tile bases + 32-bit per-lane offsets (4 A and 4 B chunks
-  //      per thread per stage); rows past the matrix edge re-read its last row
-  const uint8_t* a_base = A + (size_t)m0 * K;
-  const uint8_t* b_base = B + (size_t)n0 * K;
-  uint32_t oa[4], ob[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = (wave * 4 + i) * 64 + lane;
-    const int row = slot >> 2, c = (slot & 3) ^ bswz_pos(row);
-    const int ra = row < M - m0 ? row : M - 1 - m0;
-    const int rb = row < N - n0 ? row : N - 1 - n0;
-    oa[i] = (uint32_t)ra * (uint32_t)K + c * 16;
-    ob[i] = (uint32_t)rb * (uint32_t)K + c * 16;
-  }
-  // MX scales: wave w loads one 256-row run: w = 0,1 -> A K-blocks 2s+w; w = 2,3 -> B blocks 2s+w-2
-  const uint8_t* s_base = nullptr;
-  uint32_t os = 0;
-  int s_lim = 0;
-  if constexpr (MX) {
-    const bool isb = wave >= 2;
-    s_lim = isb ? N : M;
-    const int base_row = isb ? n0 : m0;
-    s_base = static_cast<const uint8_t*>(isb ? sb_p : sa_p) + (size_t)(wave & 1) * s_lim + base_row;
-    const int rel = lane * 4, room = s_lim - 4 - base_row;  // M, N multiples of 4 here
-    os = (uint32_t)(rel < room ? rel : room);
-  }
-  auto issue = [&](int ks, uint8_t* buf) {
-    const uint8_t* ab = a_base + (size_t)ks * BIG_BK;
-    const uint8_t* bb = b_base + (size_t)ks * BIG_BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(ab + oa[i], (lds_ptr_t)(buf + (wave * 4 + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(bb + ob[i], (lds_ptr_t)(buf + BIG_BM * BIG_BK + (wave * 4 + i) * 1024), 16, 0,
-                                       0);
-    if constexpr (MX)
-      __builtin_amdgcn_global_load_lds(s_base + (size_t)(2 * ks) * s_lim + os,
-                                       (lds_ptr_t)(buf + BIG_TILE_BYTES + wave * 256), 4, 0, 0);
-  };
-  constexpr int OPS = MX ? 9 : 8;  // vector-memory ops per thread per stage
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  auto frag = [&](const uint8_t* base, int row) -> v8i {
-    u32x4 lo = *reinterpret_cast<const u32x4*>(base + bswz(row, g));
-    u32x4 hi = *reinterpret_cast<const u32x4*>(base + bswz(row, g + 2));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  };
-  auto read_a = [&](const uint8_t* buf, int i) { return frag(buf, wm * 128 + 32 * i + r); };
-  auto read_b = [&](const uint8_t* buf, int j) { return frag(buf + BIG_BM * BIG_BK, wn * 128 + 32 * j + r); };
-
-  // A stage's operands in registers: A and B fragments and (MX) scales.
-  struct Head {
-    v8i a[4], b[4];
-    int sa[4], sb[4];
-  };
-  auto read_scales = [&](const uint8_t* buf, Head& h) {
-    if constexpr (MX) {
-      const uint8_t* sbase = buf + BIG_TILE_BYTES;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h.sa[i] = sbase[g * 256 + wm * 128 + 32 * i + r];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h.sb[j] = sbase[512 + g * 256 + wn * 128 + 32 * j + r];
-    }
-  };
-  auto row = [&](int i, const v8i& a, const Head& h) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (MX)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, h.b[j], acc[i][j], FA, FB, 0, h.sa[i], 0,
-                                                                     h.sb[j]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, h.b[j], acc[i][j], FA, FB, 0, 0, 0, 0);
-    }
-  };
-  // wait until at most `later` stages' loads are still in flight (loads retire in order)
-  auto wait_stage = [&](int later) {
-    if (later >= 3) {
-      if constexpr (OPS == 9) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    } else if (later == 2) {
-      if constexpr (OPS == 9) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else if (later == 1) {
-      if constexpr (OPS == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-  };
-
-  auto read_part1 = [&](const uint8_t* buf, Head& h) {
-    h.b[0] = read_b(buf, 0);
-    h.b[1] = read_b(buf, 1);
-    h.a[0] = read_a(buf, 0);
-    h.a[1] = read_a(buf, 1);
-  };
-  auto read_part2 = [&](const uint8_t* buf, Head& h) {
-    h.b[2] = read_b(buf, 2);
-    h.b[3] = read_b(buf, 3);
-    h.a[2] = read_a(buf, 2);
-    h.a[3] = read_a(buf, 3);
-    read_scales(buf, h);
-  };
-
-  // One pipeline stage s.  On entry (after barrier B_s): stage s's operands are in `cur`, every
-  // wave has finished reading `buf` (stage s), and stage s+1 has landed in `nbuf`.
-  //   refill `buf` with stage s+NST | read stage s+1's operands into `nxt` | 16 MFMAs of
-  //   stage s -- the DMA and LDS reads interleaved between the MFMAs so the matrix core never
-  //   waits on them | wait for stage s+2 and for the reads, barrier B_{s+1}.
-  // STEADY: stages s+1, s+2 and s+NST exist.
-  auto stage = [&](auto steady, int s, uint8_t* buf, uint8_t* nbuf, Head& cur, Head& nxt) {
-    constexpr bool STEADY = decltype(steady)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    if (STEADY || s + NST < nk) issue(s + NST, buf);
-    const bool more = STEADY || s + 1 < nk;
-    if (more) {
-      read_part1(nbuf, nxt);
-      read_part2(nbuf, nxt);
-    }
-    row(0, cur.a[0], cur);
-    row(1, cur.a[1], cur);
-    row(2, cur.a[2], cur);
-    row(3, cur.a[3], cur);
-    // interleave: per MFMA, two LDS reads and one DMA (and the address math they need)
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (LDS DMA)
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (STEADY || s + 2 < nk) {
-      if constexpr (STEADY) {
-        wait_stage(NST - 2);
-      } else {
-        const int later = (nk - 3 - s) < (NST - 2) ? (nk - 3 - s) : (NST - 2);
-        wait_stage(later);
-      }
-      lds_barrier();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  using steady_t = std::integral_constant<bool, true>;
-  using tail_t = std::integral_constant<bool, false>;
-
-  Head H0, H1;
-  if (nk > 0) {
-#pragma unroll
-    for (int s = 0; s < NST; ++s)
-      if (s < nk) issue(s, stage_buf(s));
-    wait_stage(nk - 1 < NST - 1 ? nk - 1 : NST - 1);  // stage 0 landed
-    lds_barrier();
-    read_part1(lds0, H0);
-    read_part2(lds0, H0);
-    if (nk > 1) {
-      wait_stage(nk - 2 < NST - 2 ? nk - 2 : NST - 2);  // stage 1 landed
-      lds_barrier();                                    // B_0: stage 0 fully read by every wave
-    }
-  }
-  int s = 0;
-  // steady state: every stage in this block of 4 has a successor and a refill
-  for (; s + 3 + NST < nk; s += 4) {
-    stage(steady_t{}, s, lds0, lds1, H0, H1);
-    stage(steady_t{}, s + 1, lds1, lds2, H1, H0);
-    stage(steady_t{}, s + 2, lds2, lds3, H0, H1);
-    stage(steady_t{}, s + 3, lds3, lds0, H1, H0);
-  }
-  for (; s < nk; s += 4) {
-    stage(tail_t{}, s, lds0, lds1, H0, H1);
-    if (s + 1 < nk) stage(tail_t{}, s + 1, lds1, lds2, H1, H0);
-    if (s + 2 < nk) stage(tail_t{}, s + 2, lds2, lds3, H0, H1);
-    if (s + 3 < nk) stage(tail_t{}, s + 3, lds3, lds0, H1, H0);
-  }
-
-  // ---- epilogue: C[m][n], lane holds rows 8(e/4) + 4g + e%4 of each 32x32 tile, column r
-  float scale = 1.0f;
-  if constexpr (MODE == MODE_TENSOR) scale = *static_cast<const float*>(sa_p) * *static_cast<const float*>(sb_p);
-  const bool full = m0 + BIG_BM <= M && n0 + BIG_BN <= N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + wn * 128 + 32 * j + r;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int gm = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float v = MODE == MODE_TENSOR ? acc[i][j][e] * scale : acc[i][j][e];
-        if (full || (gm < M && gn < N)) {
-          if constexpr (OUT == OUT_F32)
-            static_cast<float*>(C)[(size_t)gm * N + gn] = v;
-          else
-            static_cast<uint16_t*>(C)[(size_t)gm * N + gn] = (uint16_t)f32_to_bf16_bits(v);
-        }
-      }
-    }
-}
-
 // ------------------------------------------------------------------ ping-pong large-tile kernel
 //
-// Same 256 x 256 block tile, K step 64 and 4-stage LDS ring fed by direct-to-LDS loads as
-// above, but 8 waves in two groups of 4.  Group p computes tile rows 128p .. 128p+127; wave i
+// 256 x 256 block tile, K step 64, a 4-stage LDS ring fed by direct-to-LDS loads issued 3
+// stages ahead, and 8 waves in two groups of 4.  Group p computes tile rows 128p .. 128p+127; wave i
 // of a group computes tile columns 64i .. 64i+63 (a 128 x 64 wave tile: 4 x 2 MFMAs of
 // 32x32x64 per K step, 128 fp32 accumulators per lane).  Waves w and w+4 share a SIMD.
 //
@@ -788,7 +543,9 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   }
 
   // ---- epilogue: result register e of tile (i, j) is tile row 128p + 4(8(e/4) + 4g + e%4) + i,
-  //      column 64w + 2r + j: each lane writes column pairs (2r, 2r+1)
+  //      column 64w + 2r + j: each lane writes column pairs (2r, 2r+1).  The stores are
+  //      nontemporal: C goes on to HBM while other tiles still compute, instead of staying
+  //      dirty in the caches for whatever kernel runs next to write back.
   float scale = 1.0f;
   if constexpr (MODE == MODE_TENSOR) scale = *static_cast<const float*>(sa_p) * *static_cast<const float*>(sb_p);
   const int gn = n0 + wi * 64 + 2 * r;
@@ -808,7 +565,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
       if constexpr (OUT == OUT_F32) {
         float* c = static_cast<float*>(C) + at;
         if (pair) {
-          *reinterpret_cast<float2*>(c) = make_float2(v0, v1);
+          const u32x2 w = {__float_as_uint(v0), __float_as_uint(v1)};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(c));
         } else {
           if (gn < N) c[0] = v0;
           if (gn + 1 < N) c[1] = v1;
@@ -817,7 +575,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
         uint16_t* c = static_cast<uint16_t*>(C) + at;
         const uint32_t b0 = f32_to_bf16_bits(v0), b1 = f32_to_bf16_bits(v1);
         if (pair) {
-          *reinterpret_cast<uint32_t*>(c) = b0 | (b1 << 16);
+          __builtin_nontemporal_store(b0 | (b1 << 16), reinterpret_cast<uint32_t*>(c));
         } else {
           if (gn < N) c[0] = (uint16_t)b0;
           if (gn + 1 < N) c[1] = (uint16_t)b1;
@@ -825,8 +583,6 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
       }
     }
 }
-
-constexpr bool kUsePingPong = true;
 
 template <int MODE, int FA, int FB, int OUT>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, void* C, int M, int N, int K,
@@ -836,16 +592,15 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
     // large problems only (>= half a wave of tiles on 256 CUs); MX scale rows are read as
     // 4-byte runs, so M and N must be multiples of 4 there
     if (tiles_m * tiles_n >= 128 && M >= 4 && N >= 4 && (MODE != MODE_MX || (M % 4 == 0 && N % 4 == 0))) {
-      // the ping-pong kernel addresses a tile's rows and a stage's scale rows with 32-bit offsets
+      // the large-tile kernel addresses a tile's rows and a stage's scale rows with 32-bit
+      // offsets; beyond that the 128 x 128 kernel (64-bit addressing) takes the problem
       const int64_t mn = M > N ? M : N;
       const bool offsets32 = 256ll * K < (1ll << 32) && (MODE != MODE_MX || (int64_t)(K / 32) * mn < (1ll << 32));
-      if (kUsePingPong && offsets32)
+      if (offsets32) {
         hipLaunchKernelGGL((gemm_pp_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B, sa,
                            sb, C, M, N, K, tiles_m, tiles_n);
-      else
-        hipLaunchKernelGGL((gemm_big_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(256), 0, st, A, B, sa,
-                           sb, C, M, N, K, tiles_m, tiles_n);
-      return check_launch("fp8_gemm");
+        return check_launch("fp8_gemm");
+      }
     }
   }
   constexpr int BM = 128, BN = 128;
