@@ -284,7 +284,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // the compiler neither tracks them (it cannot tell that they never touch a stage with loads
 // in flight, and would wait for every outstanding load) nor needs registers per address.
 
-constexpr int PP_NST = 4;
 // MFMAs of a compute phase issued before its loads of the next B fragments
 constexpr int kPPLead = 2;
 // memory phase: fragment reads before the stage refill's loads
@@ -314,7 +313,14 @@ __device__ __forceinline__ uint32_t ds_read2(uint32_t vaddr) {
   return v;
 }
 
-template <int MODE, int FA, int FB, int OUT>
+// compile-time unrolling: f(integral_constant<int, I>) for I = 0 .. N-1
+template <typename F, int... Is>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
+// NST: LDS ring depth (stages in flight NST - 1 ahead); 4 x 34 KB for MX, 5 x 32 KB per tensor
+template <int MODE, int FA, int FB, int OUT, int NST>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                          const void* __restrict__ sa_p, const void* __restrict__ sb_p,
                                                          void* __restrict__ C, int M, int N, int K, int tiles_m,
@@ -324,9 +330,11 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   // same loads and the steady-state loop has no group-dependent branch
   constexpr int STAGE = BIG_TILE_BYTES + (MX ? 2 * BIG_SCALE_BYTES : 0);
   constexpr int B_OFF = BIG_BM * BIG_BK, S_OFF = BIG_TILE_BYTES;
-  static_assert(PP_NST == 4, "the main loop is unrolled for 4 stages");
-  static_assert(STAGE + B_OFF + 2048 + 16 < 65536, "stage 1 offsets must fit the LDS offset field");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[PP_NST * STAGE];
+  constexpr int D = NST - 1;                  // stages issued ahead
+  constexpr int U = NST % 2 == 0 ? NST : 2 * NST;  // unroll: stage buffer and B set both repeat
+  static_assert(NST >= 4 && NST * STAGE <= 160 * 1024, "LDS ring must fit the 160 KB of a CU");
+  static_assert(STAGE + B_OFF + 2048 + 16 < 65536, "odd stages' offsets must fit the LDS offset field");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,7 +392,10 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   };
   // wait until at most `later` stages of this wave's loads are in flight (they retire in order)
   auto wait_stage = [&](int later) {
-    if (later >= 2) {
+    if (later >= 3) {
+      if constexpr (MX) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    } else if (later == 2) {
       if constexpr (MX) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     } else if (later == 1) {
@@ -395,13 +406,14 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     }
   };
 
-  // ---- per-lane LDS base addresses; stage s, tile i adds the immediate s*STAGE + i*2048
-  //      (stages 2 and 3 from a second set of bases, to keep offsets within 16 bits)
+  // ---- per-lane LDS base addresses; stage s, tile i adds the immediate (s%2)*STAGE + i*2048
+  //      to the base set of stage pair s/2, keeping offsets within 16 bits
+  constexpr int NH = (NST + 1) / 2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t row_lo = r * 64 + ((g ^ bswz_pos(r)) << 4), row_hi = r * 64 + (((g + 2) ^ bswz_pos(r)) << 4);
-  uint32_t a_lo[2], a_hi[2], b_lo[2], b_hi[2], s_a[2], s_b[2];
+  uint32_t a_lo[NH], a_hi[NH], b_lo[NH], b_hi[NH], s_a[NH], s_b[NH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NH; ++h) {
     const uint32_t base = lds0 + h * 2 * STAGE;
     a_lo[h] = base + grp * 128 * 64 + row_lo;
     a_hi[h] = base + grp * 128 * 64 + row_hi;
@@ -426,7 +438,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   auto pack = [](const u32x4& lo, const u32x4& hi) -> v8i {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  // ST: stage buffer 0..3 (compile time); SET: B register set
+  // ST: stage buffer 0 .. NST-1 (compile time); SET: B register set
   auto read_a = [&](auto st_c) {
     constexpr int ST = decltype(st_c)::value, H = ST >> 1, O = (ST & 1) * STAGE;
     fa[0] = pack(ds_read16<O + 0 * 2048>(a_lo[H]), ds_read16<O + 0 * 2048>(a_hi[H]));
@@ -480,26 +492,23 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     __builtin_amdgcn_sched_barrier(0);
   };
   using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
 
-  // M_k then C_k for stage k in buffer ST (= k % 4), B set SET (= k % 2).  STEADY steps (stage
-  // k+3 exists) contain no branch, so the compiler keeps each phase's MFMAs between its two
-  // barriers.  The barrier closing slot 2nk-1 (group 0 after C_{nk-1}, group 1 after
+  // M_k then C_k for stage k in buffer ST (= k % NST), B set SET (= k % 2).  STEADY steps
+  // (stage k+D exists) contain no branch, so the compiler keeps each phase's MFMAs between its
+  // two barriers.  The barrier closing slot 2nk-1 (group 0 after C_{nk-1}, group 1 after
   // M_{nk-1}) and group 1's last one are dropped: no LDS is written or read after them.
   auto step = [&](auto steady, auto st_c, auto set_c, int k) {
     constexpr bool STEADY = decltype(steady)::value;
     constexpr int ST = decltype(st_c)::value, SET = decltype(set_c)::value;
-    using NextSt = std::integral_constant<int, (ST + 1) & 3>;
+    using NextSt = std::integral_constant<int, (ST + 1) % NST>;
     using NextSet = std::integral_constant<int, SET ^ 1>;
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kPPReadsFirst) {
       read_a(st_c);
       __builtin_amdgcn_sched_barrier(0);
-      if (STEADY || k + 3 < nk) issue(k + 3, (ST + 3) & 3);
+      if (STEADY || k + D < nk) issue(k + D, (ST + D) % NST);
     } else {
-      if (STEADY || k + 3 < nk) issue(k + 3, (ST + 3) & 3);
+      if (STEADY || k + D < nk) issue(k + D, (ST + D) % NST);
       __builtin_amdgcn_sched_barrier(0);
       read_a(st_c);
     }
@@ -510,9 +519,9 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     });
     __builtin_amdgcn_sched_barrier(0);  // the wait below must not split the MFMA run
     if constexpr (STEADY) {
-      wait_stage(1);  // this wave's part of stage k+2
+      wait_stage(D - 2);  // this wave's part of stage k+2
     } else {
-      if (k + 2 < nk) wait_stage(nk - k - 3 < 1 ? nk - k - 3 : 1);
+      if (k + 2 < nk) wait_stage(nk - k - 3 < D - 2 ? nk - k - 3 : D - 2);
     }
     if (STEADY || k + 1 < nk) barrier();
   };
@@ -520,26 +529,29 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   using tail_t = std::integral_constant<bool, false>;
 
   if (nk > 0) {
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    if (nk > 2) issue(2, 2);
-    wait_stage(nk - 2 < 1 ? (nk - 2 < 0 ? 0 : nk - 2) : 1);  // this wave's parts of stages 0 and 1
-    barrier();                                               // stages 0 and 1 visible
-    read_b(I0{}, I0{});                                      // stage 0's B set
-    if (grp == 1) barrier();                                 // group 1 sits out slot 0
+    unroll_seq([&](auto s_c) {
+      constexpr int S = decltype(s_c)::value;
+      if (S < nk) issue(S, S);
+    }, std::make_integer_sequence<int, D>{});
+    // this wave's parts of stages 0 and 1 landed: of the first min(D, nk) stages, the later
+    // ones may stay in flight
+    const int issued = nk < D ? nk : D, need = nk > 1 ? 2 : 1;
+    wait_stage(issued - need);
+    barrier();                  // stages 0 and 1 visible
+    read_b(I0{}, I0{});         // stage 0's B set
+    if (grp == 1) barrier();    // group 1 sits out slot 0
     int k = 0;
-    for (; k + 7 <= nk; k += 4) {  // stages k .. k+3 each have a stage 3 ahead to issue
-      step(steady_t{}, I0{}, I0{}, k);
-      step(steady_t{}, I1{}, I1{}, k + 1);
-      step(steady_t{}, I2{}, I0{}, k + 2);
-      step(steady_t{}, I3{}, I1{}, k + 3);
-    }
-    for (; k < nk; k += 4) {
-      step(tail_t{}, I0{}, I0{}, k);
-      if (k + 1 < nk) step(tail_t{}, I1{}, I1{}, k + 1);
-      if (k + 2 < nk) step(tail_t{}, I2{}, I0{}, k + 2);
-      if (k + 3 < nk) step(tail_t{}, I3{}, I1{}, k + 3);
-    }
+    for (; k + U + D <= nk; k += U)  // every step of the block has a stage D ahead to issue
+      unroll_seq([&](auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        step(steady_t{}, std::integral_constant<int, I % NST>{}, std::integral_constant<int, I % 2>{}, k + I);
+      }, std::make_integer_sequence<int, U>{});
+    for (; k < nk; k += U)
+      unroll_seq([&](auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        if (k + I < nk)
+          step(tail_t{}, std::integral_constant<int, I % NST>{}, std::integral_constant<int, I % 2>{}, k + I);
+      }, std::make_integer_sequence<int, U>{});
   }
 
   // ---- epilogue: result register e of tile (i, j) is tile row 128p + 4(8(e/4) + 4g + e%4) + i,
@@ -597,8 +609,9 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
       const int64_t mn = M > N ? M : N;
       const bool offsets32 = 256ll * K < (1ll << 32) && (MODE != MODE_MX || (int64_t)(K / 32) * mn < (1ll << 32));
       if (offsets32) {
-        hipLaunchKernelGGL((gemm_pp_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B, sa,
-                           sb, C, M, N, K, tiles_m, tiles_n);
+        constexpr int NST = 4;  // 5 stages (per tensor, 160 KB) measured no faster
+        hipLaunchKernelGGL((gemm_pp_kernel<MODE, FA, FB, OUT, NST>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+                           sa, sb, C, M, N, K, tiles_m, tiles_n);
         return check_launch("fp8_gemm");
       }
     }

@@ -15,69 +15,25 @@ namespace sfp8 {
 
 // ------------------------------------------------------------------ element loaders
 //
-// A chunk is 16 consecutive elements.  bf16: 2 x 16-byte loads; fp32: 4 x 16-byte loads.
-
+// 8 consecutive elements: one 16-byte load for bf16, two for fp32 (nontemporal: each input
+// is read once).
 template <bool BF16>
-struct Chunk16 {
-  float v[16];
-};
-
-template <bool BF16>
-__device__ __forceinline__ void load16(const void* __restrict__ base, int64_t elem, float (&v)[16], uint32_t& mx) {
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, float (&v)[8]) {
   if constexpr (BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
-    u32x4 a = __builtin_nontemporal_load(p);
-    u32x4 b = __builtin_nontemporal_load(p + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       v[2 * i] = bf16_lo(w[i]);
       v[2 * i + 1] = bf16_hi(w[i]);
-      uint32_t m = w[i] & 0x7FFF7FFFu;
-      uint32_t lo = m & 0xFFFFu, hi = m >> 16;
-      mx = mx > lo ? mx : lo;
-      mx = mx > hi ? mx : hi;
     }
   } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + elem);
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
+    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 a = __builtin_nontemporal_load(p + j);
-      v[4 * j + 0] = __uint_as_float(a.x);
-      v[4 * j + 1] = __uint_as_float(a.y);
-      v[4 * j + 2] = __uint_as_float(a.z);
-      v[4 * j + 3] = __uint_as_float(a.w);
-      uint32_t m0 = a.x & 0x7FFFFFFFu, m1 = a.y & 0x7FFFFFFFu, m2 = a.z & 0x7FFFFFFFu, m3 = a.w & 0x7FFFFFFFu;
-      m0 = m0 > m1 ? m0 : m1;
-      m2 = m2 > m3 ? m2 : m3;
-      m0 = m0 > m2 ? m0 : m2;
-      mx = mx > m0 ? mx : m0;
-    }
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
   }
-}
-
-// bits of |x| as float32 bits (bf16 maxima are tracked as 16-bit patterns)
-template <bool BF16>
-__device__ __forceinline__ uint32_t amax_f32_bits(uint32_t mx) {
-  return BF16 ? (mx << 16) : mx;
-}
-template <bool BF16>
-__device__ __forceinline__ bool has_nan(uint32_t mx) {
-  return BF16 ? (mx > 0x7F80u) : (mx > 0x7F800000u);
-}
-
-// 16 values * s -> 4 dwords of codes (NaN inputs patched when `nan` is set).
-template <int FMT>
-__device__ __forceinline__ u32x4 cast16(const float (&v)[16], float s, bool nan) {
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    w[j] = cvt4<FMT>(v[4 * j] * s, v[4 * j + 1] * s, v[4 * j + 2] * s, v[4 * j + 3] * s);
-  if (nan) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = patch_nan4(w[j], &v[4 * j]);
-  }
-  return u32x4_make(w[0], w[1], w[2], w[3]);
 }
 
 template <bool BF16>
@@ -108,13 +64,27 @@ __device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* red)
 
 // ------------------------------------------------------------------ per-tensor (delayed)
 //
-// Flat stream over n elements.  Each thread handles UNROLL chunks of 16 per iteration of a
-// grid-stride loop; amax is reduced per block and max-ed into *amax_slot with one unsigned
-// atomic per block (|x| bits of non-negative floats order like the floats; NaN wins).
+// Flat stream over n elements in pieces of 8 (16 bytes of bf16).  A block takes 2 x 256
+// pieces per pass of a grid-stride loop; the pieces of one load instruction are consecutive
+// across the wave's lanes, so every instruction reads 1 KB (bf16) contiguous.  amax is
+// reduced per block and max-ed into *amax_slot with one unsigned atomic per block (|x| bits
+// of non-negative floats order like the floats; NaN wins).
 
 constexpr int kTensorThreads = 256;
-constexpr int kTensorUnroll = 1;
+constexpr int kTensorPieces = 2;
 constexpr int64_t kTensorMaxBlocks = 32768;
+
+// 8 values * s -> 8 codes (NaN inputs patched)
+template <int FMT>
+__device__ __forceinline__ u32x2 cast8(const float (&v)[8], float s, uint32_t amax_bits) {
+  uint32_t w0 = cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+  uint32_t w1 = cvt4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+  if (amax_bits > 0x7F800000u) {
+    w0 = patch_nan4(w0, &v[0]);
+    w1 = patch_nan4(w1, &v[4]);
+  }
+  return u32x2{w0, w1};
+}
 
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void* __restrict__ x, int64_t n,
@@ -123,37 +93,34 @@ __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void
                                                                       uint8_t* __restrict__ q) {
   __shared__ uint32_t red[4];
   const float s = *scale_p;
-  const int64_t nchunks = n >> 4;
-  const int64_t stride = (int64_t)gridDim.x * kTensorThreads;
-  uint32_t mx = 0;
-  int64_t c = (int64_t)blockIdx.x * kTensorThreads + threadIdx.x;
-  for (; c + (kTensorUnroll - 1) * stride < nchunks; c += kTensorUnroll * stride) {
-    float v[kTensorUnroll][16];
-    uint32_t m[kTensorUnroll];
+  const int64_t npieces = n >> 3;
+  const int64_t step = (int64_t)gridDim.x * kTensorThreads * kTensorPieces;
+  uint32_t mxf = 0;
+  for (int64_t b = (int64_t)blockIdx.x * kTensorThreads * kTensorPieces; b < npieces; b += step) {
+    float v[kTensorPieces][8];
 #pragma unroll
-    for (int u = 0; u < kTensorUnroll; ++u) {
-      m[u] = 0;
-      load16<BF16>(x, (c + u * stride) << 4, v[u], m[u]);
+    for (int j = 0; j < kTensorPieces; ++j) {
+      const int64_t pc = b + j * kTensorThreads + threadIdx.x;
+      if (pc < npieces) load8<BF16>(x, pc << 3, v[j]);
     }
 #pragma unroll
-    for (int u = 0; u < kTensorUnroll; ++u) {
-      u32x4 o = cast16<FMT>(v[u], s, has_nan<BF16>(m[u]));
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q + ((c + u * stride) << 4)));
-      mx = mx > m[u] ? mx : m[u];
+    for (int j = 0; j < kTensorPieces; ++j) {
+      const int64_t pc = b + j * kTensorThreads + threadIdx.x;
+      if (pc < npieces) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t a = abs_bits(v[j][i]);
+          m = m > a ? m : a;
+        }
+        __builtin_nontemporal_store(cast8<FMT>(v[j], s, m), reinterpret_cast<u32x2*>(q + (pc << 3)));
+        mxf = mxf > m ? mxf : m;
+      }
     }
   }
-  for (; c < nchunks; c += stride) {
-    float v[16];
-    uint32_t m = 0;
-    load16<BF16>(x, c << 4, v, m);
-    u32x4 o = cast16<FMT>(v, s, has_nan<BF16>(m));
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q + (c << 4)));
-    mx = mx > m ? mx : m;
-  }
-  uint32_t mxf = amax_f32_bits<BF16>(mx);
-  // tail (n % 16 elements): block 0
-  if (blockIdx.x == 0 && threadIdx.x < (n & 15)) {
-    const int64_t i = (nchunks << 4) + threadIdx.x;
+  // tail (n % 8 elements): block 0
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t i = (npieces << 3) + threadIdx.x;
     float xv = load_one<BF16>(x, i);
     q[i] = cast_one<FMT>(xv, s);
     uint32_t a = abs_bits(xv);
@@ -168,100 +135,127 @@ __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void
 
 // ------------------------------------------------------------------ 1x128 tiles
 //
-// One 16-lane group per 1x128 run: 8 elements per lane, amax over the group, s = fmax/amax,
-// cast, and scale_inv written at [kb][row] (kb-major, so consecutive rows of one kb are
-// contiguous: a block covers 16 consecutive rows of one kb).
+// One 16-lane group per 1x128 run (8 elements per lane): amax over the group, s = fmax/amax,
+// cast.  A block covers 16 rows x 4 runs (512 columns); wave w takes rows 4w..4w+3 of it, so
+// each lane has four rows' loads in flight and each wave reads 1 KB row segments.
+// Consecutive blocks walk the input in address order.  scale_inv is [kb][row] (kb-major, so
+// one K step of the GEMM reads a contiguous vector of rows); the block's 4 x 16 values are
+// staged in LDS and leave as 64-byte rows of that layout.
+
+constexpr int kTileRowsPerWave = 4;
+constexpr int kTileRows = 4 * kTileRowsPerWave;
 
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(256) quant_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                          uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
-  const int64_t run = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // run id = kb * rows + row
+  __shared__ float sinv_s[4][kTileRows];
   const int64_t nkb = cols >> 7;
-  if (run >= nkb * rows) return;
-  const int64_t kb = run / rows, row = run - kb * rows;
-  const int lane16 = threadIdx.x & 15;
-  const int64_t e0 = row * cols + kb * 128 + lane16 * 8;
-  float v[8];
-  uint32_t mx = 0;
-  if constexpr (BF16) {
-    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
-    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  const int64_t ncb = (nkb + 3) >> 2;
+  const int64_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrun = lane >> 4, lane16 = lane & 15;
+  const int64_t kb = cb * 4 + lrun;
+  const int64_t row0 = rb * kTileRows + wave * kTileRowsPerWave;
+  if (kb < nkb) {  // whole 16-lane groups take the same branch
+    const int64_t c0 = kb * 128 + lane16 * 8;
+    float v[kTileRowsPerWave][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
+    for (int j = 0; j < kTileRowsPerWave; ++j)
+      if (row0 + j < rows) load8<BF16>(x, (row0 + j) * cols + c0, v[j]);
+#pragma unroll
+    for (int j = 0; j < kTileRowsPerWave; ++j) {
+      if (row0 + j >= rows) break;
+      uint32_t mx = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = abs_bits(v[j][i]);
+        mx = mx > a ? mx : a;
+      }
+      const bool nan_here = mx > 0x7F800000u;
+      mx = group_max_u32<16>(mx);
+      float s, s_inv;
+      current_scale<FMT>(mx, s, s_inv);
+      uint32_t w0 = cvt4<FMT>(v[j][0] * s, v[j][1] * s, v[j][2] * s, v[j][3] * s);
+      uint32_t w1 = cvt4<FMT>(v[j][4] * s, v[j][5] * s, v[j][6] * s, v[j][7] * s);
+      if (nan_here) {
+        w0 = patch_nan4(w0, &v[j][0]);
+        w1 = patch_nan4(w1, &v[j][4]);
+      }
+      const u32x2 o = {w0, w1};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(q + (row0 + j) * cols + c0));
+      if (lane16 == 0) sinv_s[lrun][wave * kTileRowsPerWave + j] = s_inv;
     }
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
-    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t a = abs_bits(v[i]);
-    mx = mx > a ? mx : a;
+  __syncthreads();
+  if (threadIdx.x < 4 * kTileRows) {
+    const int lr = threadIdx.x / kTileRows, rr = threadIdx.x - lr * kTileRows;
+    const int64_t kbx = cb * 4 + lr, row = rb * kTileRows + rr;
+    if (kbx < nkb && row < rows) sinv_out[kbx * rows + row] = sinv_s[lr][rr];
   }
-  const bool nan_here = mx > 0x7F800000u;
-  mx = group_max_u32<16>(mx);
-  float s, s_inv;
-  current_scale<FMT>(mx, s, s_inv);
-  uint32_t w0 = cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-  uint32_t w1 = cvt4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
-  if (nan_here) {
-    w0 = patch_nan4(w0, &v[0]);
-    w1 = patch_nan4(w1, &v[4]);
-  }
-  *reinterpret_cast<uint2*>(q + e0) = make_uint2(w0, w1);
-  if (lane16 == 0) sinv_out[kb * rows + row] = s_inv;
 }
 
 // ------------------------------------------------------------------ 128x128 blocks
 //
-// One 256-thread block per 128x128 block: thread t covers row t/2, columns 64*(t%2)..+64 of
-// the block, held in registers through the block reduction.  A partial last row-block uses
-// the rows present (absent rows contribute nothing).
+// One 1024-thread block per 128 x 512 region (four 128x128 scale blocks side by side): wave w
+// takes rows 8w..8w+7, and on each row its 64 lanes read 512 consecutive elements (16 lanes
+// per scale block), so every load instruction reads 1 KB of bf16 contiguous.  The values stay
+// in registers through the reduction (16-lane shuffles, then across the 16 waves in LDS).
+// Consecutive blocks walk the input in address order.  A partial last row block uses the
+// rows present (absent rows contribute nothing).
+
+constexpr int kBlockThreads = 1024;
+constexpr int kBlockRowsPerWave = 8;
 
 template <int FMT, bool BF16>
-__global__ void __launch_bounds__(256) quant_block_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                          uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
-  __shared__ uint32_t red[4];
+__global__ void __launch_bounds__(kBlockThreads) quant_block_kernel(const void* __restrict__ x, int64_t rows,
+                                                                   int64_t cols, uint8_t* __restrict__ q,
+                                                                   float* __restrict__ sinv_out) {
+  __shared__ uint32_t red[16][4];
   const int64_t nkb = cols >> 7;
-  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
-  const int64_t row = rb * 128 + (threadIdx.x >> 1);
-  const bool valid = row < rows;
-  const int64_t e0 = row * cols + kb * 128 + (threadIdx.x & 1) * 64;
-  float v[64];
-  uint32_t mx = 0;
-  if (valid) {
+  const int64_t ncb = (nkb + 3) >> 2;
+  const int64_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4;  // scale block within the region
+  const int64_t kb = cb * 4 + grp;
+  const int64_t row0 = rb * 128 + wave * kBlockRowsPerWave;
+  const int64_t c0 = kb * 128 + (lane & 15) * 8;
+  const bool col_ok = kb < nkb;  // whole 16-lane groups
+  float v[kBlockRowsPerWave][8];
+  uint32_t m[kBlockRowsPerWave], mx = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float t[16];
-      load16<BF16>(x, e0 + 16 * c, t, mx);
+  for (int j = 0; j < kBlockRowsPerWave; ++j) {
+    if (col_ok && row0 + j < rows) {
+      load8<BF16>(x, (row0 + j) * cols + c0, v[j]);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[16 * c + i] = t[i];
+      for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = 0.0f;
   }
-  const uint32_t mine = amax_f32_bits<BF16>(mx);
-  const uint32_t bm = block_max_u32_256(mine, red);
+#pragma unroll
+  for (int j = 0; j < kBlockRowsPerWave; ++j) {
+    m[j] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = abs_bits(v[j][i]);
+      m[j] = m[j] > a ? m[j] : a;
+    }
+    mx = mx > m[j] ? mx : m[j];
+  }
+  mx = group_max_u32<16>(mx);
+  if ((lane & 15) == 0) red[wave][grp] = mx;
+  __syncthreads();
+  uint32_t bm = red[0][grp];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) bm = bm > red[w][grp] ? bm : red[w][grp];
   float s, s_inv;
   current_scale<FMT>(bm, s, s_inv);
-  if (valid) {
-    const bool nan_here = has_nan<BF16>(mx);
+  if (col_ok) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float t[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t[i] = v[16 * c + i];
-      u32x4 o = cast16<FMT>(t, s, nan_here);
-      *reinterpret_cast<u32x4*>(q + e0 + 16 * c) = o;
-    }
+    for (int j = 0; j < kBlockRowsPerWave; ++j)
+      if (row0 + j < rows)
+        __builtin_nontemporal_store(cast8<FMT>(v[j], s, m[j]), reinterpret_cast<u32x2*>(q + (row0 + j) * cols + c0));
+    if (wave == 0 && (lane & 15) == 0) sinv_out[rb * nkb + kb] = s_inv;
   }
-  if (threadIdx.x == 0) sinv_out[rb * nkb + kb] = s_inv;
 }
 
 // ------------------------------------------------------------------ MX 1x32
@@ -304,24 +298,6 @@ constexpr int kMxRowsPerWave = 2;
 constexpr int kMxRows = 4 * kMxRowsPerWave;
 constexpr int kMxRuns = 16;
 
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, float (&v)[8]) {
-  if constexpr (BF16) {
-    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
-    uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
-    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
-  }
-}
 
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(256) quant_mx_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
@@ -381,20 +357,20 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
                         uint8_t* q, void* sinv, hipStream_t st) {
   const int64_t n = rows * cols;
   if (gran == FP8_SCALE_TENSOR) {
-    const int64_t nchunks = n >> 4;
-    int64_t blocks = (nchunks + kTensorThreads * kTensorUnroll - 1) / (kTensorThreads * kTensorUnroll);
+    const int64_t per_block = (int64_t)kTensorThreads * kTensorPieces * 8;
+    int64_t blocks = (n + per_block - 1) / per_block;
     if (blocks < 1) blocks = 1;
     if (blocks > kTensorMaxBlocks) blocks = kTensorMaxBlocks;
     hipLaunchKernelGGL((quant_tensor_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(kTensorThreads), 0, st, x, n,
                        scale, reinterpret_cast<uint32_t*>(amax_slot), q);
   } else if (gran == FP8_SCALE_TILE_1x128) {
-    const int64_t runs = rows * (cols >> 7);
-    hipLaunchKernelGGL((quant_tile_kernel<FMT, BF16>), dim3((unsigned)((runs + 15) / 16)), dim3(256), 0, st, x, rows,
-                       cols, q, static_cast<float*>(sinv));
-  } else if (gran == FP8_SCALE_BLOCK_128x128) {
-    const int64_t blocks = ((rows + 127) / 128) * (cols >> 7);
-    hipLaunchKernelGGL((quant_block_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
+    const int64_t blocks = ((rows + kTileRows - 1) / kTileRows) * (((cols >> 7) + 3) / 4);
+    hipLaunchKernelGGL((quant_tile_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
                        static_cast<float*>(sinv));
+  } else if (gran == FP8_SCALE_BLOCK_128x128) {
+    const int64_t blocks = ((rows + 127) / 128) * (((cols >> 7) + 3) / 4);
+    hipLaunchKernelGGL((quant_block_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, x, rows,
+                       cols, q, static_cast<float*>(sinv));
   } else {
     const int64_t blocks = ((rows + kMxRows - 1) / kMxRows) * (((cols >> 5) + kMxRuns - 1) / kMxRuns);
     hipLaunchKernelGGL((quant_mx_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
