@@ -596,6 +596,269 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
     }
 }
 
+// ------------------------------------------------------------------ blockwise large-tile kernel
+//
+// 1x128 activation tiles x 128x128 weight blocks (DeepSeek-V3 style scaling, per the course
+// page's absmax bullet): every 128-K block's partial product is scaled by
+// sa[kb][m] * sb[n/128][kb] and added into an fp32 accumulator.  The K step is one scale
+// block (128), so each 16x16x128 MFMA computes a whole block's partial for a 16 x 16 tile
+// from zero, and the partial goes straight into the accumulator with one fma: no second set
+// of accumulators is needed.
+//
+// Block tile 256 x 128 (one weight block column), 3-stage LDS ring of 50 KB (A 256 x 128 B,
+// B 128 x 128 B, the stage's 256 row scales, copies of its weight-block scale), filled by
+// direct-to-LDS loads 2 stages ahead.  8 waves: group p = wave / 4 holds tile rows
+// 128p .. 128p+127; wave i of a group takes the 64 x 64 slab at rows 64 (i / 2), columns
+// 64 (i % 2): 4 x 4 tiles of 16x16, 64 fp32 accumulators per lane.  Same ping-pong as the
+// kernel above (memory phase: this wave's loads of stage k+2, all of stage k's fragments and
+// scales; compute phase: 16 MFMAs and 64 fmas), with group 1 one barrier behind.
+//
+// 16x16x128 operand layout: lane l = 16 g + r supplies row r; its 32 bytes are K = 16g..16g+15
+// and K = 64+16g..64+16g+15; result register jj of lane l is C[4g + jj][r].
+// Row interleave: tile i's MFMA row t is slab row 4t + i, tile j's column t is slab column
+// 4t + j (the DMA places them at LDS rows 16i + t / 16j + t).  A lane's 16 accumulator rows
+// (16g + 4jj + i) are then 16 consecutive rows, whose scales are one 64-byte LDS read, and its
+// 4 columns per row (4r + j) leave as one 8-byte (bf16) or 16-byte (fp32) store.
+
+constexpr int BLK_BM = 256, BLK_BN = 128, BLK_BK = 128;
+constexpr int BLK_B_OFF = BLK_BM * BLK_BK;               // 32 KB of A
+constexpr int BLK_SA_OFF = BLK_B_OFF + BLK_BN * BLK_BK;  // 16 KB of B
+constexpr int BLK_SB_OFF = BLK_SA_OFF + 1024;            // 256 row scales
+constexpr int BLK_STAGE = BLK_SB_OFF + 1024;             // 4 copies x 64 of the block scale
+constexpr int BLK_NST = 3;
+
+// the tile row held at LDS row q of a 64-row slab layout (tile i's MFMA row t at 16i + t is
+// slab row 4t + i)
+__device__ __forceinline__ int blk_row_of(int q) { return (q & ~63) + 4 * (q & 15) + ((q >> 4) & 3); }
+// position of 16-byte chunk c in 128-byte LDS row q (the small-tile kernel's swizzle)
+__device__ __forceinline__ int blk_pos(int q, int c) { return c ^ (((q >> 1) ^ ((q & 1) << 2)) & 7); }
+
+template <int FA, int FB, int OUT>
+__global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                          const float* __restrict__ sa_p,
+                                                          const float* __restrict__ sb_p, void* __restrict__ C, int M,
+                                                          int N, int K, int tiles_m, int tiles_n) {
+  constexpr int STAGE = BLK_STAGE, NST = BLK_NST, D = NST - 1, U = NST;
+  static_assert(NST * STAGE <= 160 * 1024, "LDS ring must fit the 160 KB of a CU");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wi = wave & 3, wr = wi >> 1, wc = wi & 1;
+  const int g = lane >> 4, r = lane & 15;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BLK_BM, n0 = tn * BLK_BN;
+  const int nk = K / BLK_BK;
+
+  // ---- loads: 48 x 1 KB of tile data per stage, 6 per wave (ops 0..31 are A, 32..47 B), and
+  //      one scale load per wave (waves 0-3: 64 row scales each; 4-7: a copy of the block scale)
+  const int lim_a = M - m0, lim_b = N - n0;
+  const uint64_t a_bytes = (uint64_t)lim_a * K, b_bytes = (uint64_t)lim_b * K;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(A + (size_t)m0 * K), (short)0, (int)(a_bytes < 0xFFFFFFFFull ? a_bytes : 0xFFFFFFFFull),
+      kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(B + (size_t)n0 * K), (short)0, (int)(b_bytes < 0xFFFFFFFFull ? b_bytes : 0xFFFFFFFFull),
+      kBufferFlags);
+  uint32_t od[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int o = wave * 6 + i, local = o < 32 ? o : o - 32;
+    const int slot = local * 64 + lane, q = slot >> 3, c = blk_pos(q, slot & 7);
+    const int row = blk_row_of(q), lim = o < 32 ? lim_a : lim_b;
+    od[i] = (uint32_t)(row < lim ? row : lim - 1) * (uint32_t)K + c * 16;
+  }
+  const int nkb = nk;
+  const bool s_is_a = wave < 4;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t s_voff;
+  if (s_is_a) {
+    const uint64_t bytes = ((uint64_t)nkb * M - m0) * 4;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sa_p + m0), (short)0,
+                                           (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
+    const int row = wave * 64 + lane;
+    s_voff = (uint32_t)(row < lim_a ? row : lim_a - 1) * 4;
+  } else {
+    const uint64_t bytes = ((uint64_t)tiles_n * nkb - (uint64_t)tn * nkb) * 4;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb_p + (size_t)tn * nkb), (short)0,
+                                           (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
+    s_voff = 0;
+  }
+  const int s_lds = s_is_a ? BLK_SA_OFF + wave * 256 : BLK_SB_OFF + (wave - 4) * 256;
+  const uint32_t s_step = s_is_a ? (uint32_t)M * 4 : 4;
+  auto issue = [&](int ks, int st) {
+    uint8_t* buf = smem + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave * 6 + i < 32 ? ra : rb, (lds_ptr_t)(buf + (wave * 6 + i) * 1024), 16,
+                                               od[i], ks * BLK_BK, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(buf + s_lds), 4, s_voff, ks * s_step, 0, 0);
+  };
+  // wait until at most `later` stages of this wave's loads (7 per stage) are in flight
+  auto wait_stage = [&](int later) {
+    if (later >= 1) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // ---- per-lane LDS bases per stage (immediates add the tile offsets)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const int slab_a = grp * 128 + wr * 64, slab_b = wc * 64;
+  uint32_t a_lo[NST], a_hi[NST], b_lo[NST], b_hi[NST], s_a[NST], s_b[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const uint32_t base = lds0 + st * STAGE;
+    const int qa = slab_a + r, qb = slab_b + r;  // tile 0's rows; tile i adds 16 rows = 2048 B
+    a_lo[st] = base + qa * 128 + (blk_pos(qa, g) << 4);
+    a_hi[st] = base + qa * 128 + (blk_pos(qa, g + 4) << 4);
+    b_lo[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g) << 4);
+    b_hi[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g + 4) << 4);
+    s_a[st] = base + BLK_SA_OFF + (slab_a + 16 * g) * 4;
+    s_b[st] = base + BLK_SB_OFF;
+  }
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i fa[4], fb[4];
+  float fsa[16], fsb = 0.f;
+  auto pack = [](const u32x4& lo, const u32x4& hi) -> v8i {
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto read_all = [&](auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
+    // rows 16i + r of the slab: blk_pos depends on bits 0-3 of the row only, so tile i is the
+    // same lane address + 16 rows of 128 B
+    fa[0] = pack(ds_read16<0 * 2048>(a_lo[ST]), ds_read16<0 * 2048>(a_hi[ST]));
+    fa[1] = pack(ds_read16<1 * 2048>(a_lo[ST]), ds_read16<1 * 2048>(a_hi[ST]));
+    fa[2] = pack(ds_read16<2 * 2048>(a_lo[ST]), ds_read16<2 * 2048>(a_hi[ST]));
+    fa[3] = pack(ds_read16<3 * 2048>(a_lo[ST]), ds_read16<3 * 2048>(a_hi[ST]));
+    fb[0] = pack(ds_read16<0 * 2048>(b_lo[ST]), ds_read16<0 * 2048>(b_hi[ST]));
+    fb[1] = pack(ds_read16<1 * 2048>(b_lo[ST]), ds_read16<1 * 2048>(b_hi[ST]));
+    fb[2] = pack(ds_read16<2 * 2048>(b_lo[ST]), ds_read16<2 * 2048>(b_hi[ST]));
+    fb[3] = pack(ds_read16<3 * 2048>(b_lo[ST]), ds_read16<3 * 2048>(b_hi[ST]));
+    const u32x4 s0 = ds_read16<0>(s_a[ST]), s1 = ds_read16<16>(s_a[ST]), s2 = ds_read16<32>(s_a[ST]),
+                s3 = ds_read16<48>(s_a[ST]);
+    const u32x4 sv[4] = {s0, s1, s2, s3};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      fsa[4 * h + 0] = __uint_as_float(sv[h].x);
+      fsa[4 * h + 1] = __uint_as_float(sv[h].y);
+      fsa[4 * h + 2] = __uint_as_float(sv[h].z);
+      fsa[4 * h + 3] = __uint_as_float(sv[h].w);
+    }
+    fsb = __uint_as_float(ds_read4<0>(s_b[ST]));
+  };
+  // 16 MFMAs, each partial folded into its accumulators two MFMAs later:
+  // acc[i][j][jj] += p * (sa[row 16g + 4jj + i] * sb)
+  auto compute = [&]() {
+    float sab[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sab[e] = fsa[e] * fsb;
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    v4f p[16];
+    auto fold = [&](int t) {
+      const int i = t >> 2, j = t & 3;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = fmaf(p[t][jj], sab[4 * jj + i], acc[i][j][jj]);
+    };
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      p[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t >> 2], fb[t & 3], zero, FA, FB, 0, 0, 0, 0);
+      if (t >= 2) fold(t - 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fold(14);
+    fold(15);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // M_k then C_k for stage k in buffer ST = k % 3; the last barriers are dropped as in the
+  // kernel above
+  auto step = [&](auto steady, auto st_c, int k) {
+    constexpr bool STEADY = decltype(steady)::value;
+    constexpr int ST = decltype(st_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    read_all(st_c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (STEADY || k + D < nk) issue(k + D, (ST + D) % NST);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (STEADY) {
+      wait_stage(1);  // this wave's part of stage k+1
+    } else {
+      if (k + 1 < nk) wait_stage(nk - k - 2 < 1 ? nk - k - 2 : 1);
+    }
+    if (STEADY || !(grp == 1 && k + 1 == nk)) barrier();
+    compute();
+    __builtin_amdgcn_sched_barrier(0);
+    if (STEADY || k + 1 < nk) barrier();
+  };
+  using steady_t = std::integral_constant<bool, true>;
+  using tail_t = std::integral_constant<bool, false>;
+
+  if (nk > 0) {
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    wait_stage(nk > 1 ? 1 : 0);  // this wave's part of stage 0
+    barrier();                   // stage 0 visible
+    if (grp == 1) barrier();     // group 1 sits out slot 0
+    int k = 0;
+    for (; k + U + D <= nk; k += U)
+      unroll_seq([&](auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        step(steady_t{}, std::integral_constant<int, I>{}, k + I);
+      }, std::make_integer_sequence<int, U>{});
+    for (; k < nk; k += U)
+      unroll_seq([&](auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        if (k + I < nk) step(tail_t{}, std::integral_constant<int, I>{}, k + I);
+      }, std::make_integer_sequence<int, U>{});
+  }
+
+  // ---- epilogue: acc[i][j][jj] is tile row slab + 16g + 4jj + i, column slab + 4r + j
+  const int gn = n0 + slab_b + 4 * r;
+  const bool quad = (N & 3) == 0 && gn + 3 < N;  // all four columns present, store aligned
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gm = m0 + slab_a + 16 * g + 4 * jj + i;
+      if (gm >= M) continue;
+      const float v0 = acc[i][0][jj], v1 = acc[i][1][jj], v2 = acc[i][2][jj], v3 = acc[i][3][jj];
+      const size_t at = (size_t)gm * N + gn;
+      if constexpr (OUT == OUT_F32) {
+        float* c = static_cast<float*>(C) + at;
+        if (quad) {
+          const u32x4 w = u32x4_make(__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3));
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(c));
+        } else {
+          if (gn < N) c[0] = v0;
+          if (gn + 1 < N) c[1] = v1;
+          if (gn + 2 < N) c[2] = v2;
+          if (gn + 3 < N) c[3] = v3;
+        }
+      } else {
+        uint16_t* c = static_cast<uint16_t*>(C) + at;
+        const uint32_t b0 = f32_to_bf16_bits(v0), b1 = f32_to_bf16_bits(v1), b2 = f32_to_bf16_bits(v2),
+                       b3 = f32_to_bf16_bits(v3);
+        if (quad) {
+          const u32x2 w = {b0 | (b1 << 16), b2 | (b3 << 16)};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(c));
+        } else {
+          if (gn < N) c[0] = (uint16_t)b0;
+          if (gn + 1 < N) c[1] = (uint16_t)b1;
+          if (gn + 2 < N) c[2] = (uint16_t)b2;
+          if (gn + 3 < N) c[3] = (uint16_t)b3;
+        }
+      }
+    }
+}
+
 template <int MODE, int FA, int FB, int OUT>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, void* C, int M, int N, int K,
                        hipStream_t st) {
@@ -614,6 +877,16 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
                            sa, sb, C, M, N, K, tiles_m, tiles_n);
         return check_launch("fp8_gemm");
       }
+    }
+  }
+  if constexpr (MODE == MODE_BLOCK) {
+    const int tiles_m = (M + BLK_BM - 1) / BLK_BM, tiles_n = (N + BLK_BN - 1) / BLK_BN;
+    // large problems only; 32-bit offsets for a tile's rows and a stage's scales
+    const bool offsets32 = 256ll * K < (1ll << 32) && (int64_t)(K / 128) * M * 4 < (1ll << 32);
+    if (tiles_m * tiles_n >= 128 && offsets32) {
+      hipLaunchKernelGGL((gemm_blk_kernel<FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+                         static_cast<const float*>(sa), static_cast<const float*>(sb), C, M, N, K, tiles_m, tiles_n);
+      return check_launch("fp8_gemm");
     }
   }
   constexpr int BM = 128, BN = 128;

@@ -177,3 +177,29 @@ def test_large_tile_kernel(sq, mnk, mode):
         r[-1] = M - 1
         Cr, S, G = og.gemm_ref(A, 0, ea, og.MX_1x32, B, 0, eb, og.MX_1x32, rows=r)
         check_gemm(np_of(C)[r], Cr, S, G, K, "mx", False, f"large mx {mnk}")
+
+
+# Blockwise shapes with >= 128 tiles of 256 x 128 run on the large-tile blockwise kernel:
+# ragged M and N (N odd takes the unpaired epilogue), K steps fewer than and not a multiple
+# of the pipeline depth.
+BIG_BLOCK_CASES = [(2085, 4100, 384), (2048, 4097, 1152), (4096, 2304, 256), (1300, 3000, 128)]
+
+
+@pytest.mark.parametrize("out", [0, 1])
+@pytest.mark.parametrize("mnk", BIG_BLOCK_CASES)
+def test_large_tile_blockwise(sq, mnk, out):
+    M, N, K = mnk
+    announce("large-tile blockwise gemm", out, mnk)
+    rng = np.random.default_rng(M + 3 * N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp2(rng.integers(-6, 6, (M, 1))).astype(np.float32)
+    x.flat[rng.integers(0, x.size, max(1, x.size // 1000))] *= 100.0
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[:, :128] *= 50.0  # one weight block column with a much larger scale
+    A, sa = oq.quantize_tile_1x128(x, 0)
+    B, sb = oq.quantize_block_128x128(w, 0)
+    C = sq.fp8_gemm(_t(A), 0, _t(sa), sq.FP8_SCALE_TILE_1x128, _t(B), 0, _t(sb), sq.FP8_SCALE_BLOCK_128x128, out)
+    torch.cuda.synchronize()
+    r = np.sort(rng.choice(M, 192, replace=False))
+    r[-1] = M - 1
+    Cr, S, G = og.gemm_ref(A, 0, sa, og.TILE_1x128, B, 0, sb, og.BLOCK_128x128, rows=r)
+    check_gemm(np_of(C)[r], Cr, S, G, K, "block", out == 1, f"large blockwise {mnk} out{out}")
