@@ -152,6 +152,37 @@ int fp8_cast_transpose(const void *x, int x_dtype, int64_t rows, int64_t cols, i
                        void *stream);
 
 /*
+ * fp8_cast_transpose_blockwise -- current-scaling cast plus its transpose in one pass, each
+ *   copy with the scales its backward GEMM needs.
+ *   [W] absmax bullet (DeepSeek-V3: scales per 128 activation values and per 128x128 weight
+ *   block, computed from the current block); the backward GEMMs multiply by transposed
+ *   operands, and keeping them K-contiguous (TN) means the transposed copy needs runs along
+ *   its own K (the source's rows).
+ *
+ *   x             device, x_dtype HP_F32 or HP_BF16, [rows][cols]
+ *   granularity   FP8_SCALE_TILE_1x128 or FP8_SCALE_BLOCK_128x128
+ *   q             device uint8 [rows][cols]
+ *   qT            device uint8 [cols][rows]
+ *   TILE_1x128:   q exactly as fp8_quantize(TILE_1x128): one scale per 1x128 run of a row,
+ *                 q_scale_inv = fp32 [cols/128][rows];
+ *                 qT = the codes of x^T with one scale per 1x128 run of x^T's rows (a 128x1
+ *                 run of a source column), qT_scale_inv = fp32 [rows/128][cols]
+ *                 (for wgrad: dW = dY^T X with A = dY^T, B = X^T, both TILE_1x128).
+ *   BLOCK_128x128: q exactly as fp8_quantize(BLOCK_128x128), q_scale_inv = fp32
+ *                 [rows/128][cols/128]; qT[c][r] = q[r][c] and qT_scale_inv = fp32
+ *                 [cols/128][rows/128], its transpose (for dgrad: dX = dY W with B = W^T).
+ *   Element rule as fp8_quantize (s = fmax / amax of the run or block, zero or non-finite
+ *   amax -> 1, one fp32 multiply, saturating RNE cast, NaN -> sign | 0x7F).
+ *   rows % 128 == 0 and cols % 128 == 0.  Empty inputs are a no-op.
+ *   Alignment: x, q, qT 16-byte aligned; scale arrays 4-byte aligned.
+ *   Errors: FP8_ERR_ARG (null pointer, bad enum, misalignment), FP8_ERR_SHAPE (rows or cols
+ *           not a multiple of 128), FP8_ERR_DTYPE (x_dtype).
+ */
+int fp8_cast_transpose_blockwise(const void *x, int x_dtype, int64_t rows, int64_t cols, int fmt,
+                                 int granularity, uint8_t *q, float *q_scale_inv, uint8_t *qT,
+                                 float *qT_scale_inv, void *stream);
+
+/*
  * fp8_gemm -- C[M][N] = sum_k deq(A[m][k]) * deq(B[n][k])  (C = A . B^T, Y = X W^T).
  *   [W] FP8 bullet (matmuls run in FP8) and accumulation-precision bullet (FP8 products are
  *   summed in a wider accumulator and partial sums are promoted to fp32 at fixed
@@ -165,7 +196,10 @@ int fp8_cast_transpose(const void *x, int x_dtype, int64_t rows, int64_t cols, i
  *                        [ceil(N/128)][K/128]; each 128-long K block's partial sum is
  *                        multiplied by sa[kb][m] * sb[n/128][kb] and added to an fp32
  *                        accumulator (promotion every 128 K).
- *     MX_1x32 x MX_1x32: a_scale_inv = uint8 e8m0 [K/32][M], b_scale_inv = uint8 e8m0
+ *     TILE_1x128 x TILE_1x128: a_scale_inv = fp32 [K/128][M], b_scale_inv = fp32 [K/128][N];
+                        each K block's partial sum is multiplied by sa[kb][m] * sb[kb][n]
+                        (the blockwise wgrad, both operands activation-style runs).
+     MX_1x32 x MX_1x32: a_scale_inv = uint8 e8m0 [K/32][M], b_scale_inv = uint8 e8m0
  *                        [K/32][N] (as fp8_quantize writes them); the matrix cores apply
  *                        2^(ea - 127) * 2^(eb - 127) per 32-long run.
  *   Products are exact; the matrix cores sum runs of 8 products in a fixed-point window

@@ -22,6 +22,13 @@ used a scale for every 128 activation values and every 128 x 128 weight block):
 
 Cast-transpose returns the same bytes as the per-tensor quantizer and their
 transpose: qT[c][r] = q[r][c].
+
+Blockwise cast-transpose (the blockwise recipe's backward operands): the
+transposed copy carries the scales of its own contraction axis, which is the
+source's row axis.  For 1x128 tiles, the copy of x^T is quantised in runs of
+128 consecutive source rows of one column (a 128x1 run of x, a 1x128 run of
+x^T); for 128x128 blocks the block, and so its scale, is the same either way
+round, so the copy is the transpose of the codes and of the scale matrix.
 """
 
 from __future__ import annotations
@@ -97,3 +104,34 @@ def cast_transpose(x, scale, fmt):
     """Per-tensor quantisation plus the transposed bytes -> (q, qT, amax)."""
     q, a = quantize_tensor(x, scale, fmt)
     return q, np.ascontiguousarray(q.T), a
+
+
+def quantize_tile_128x1(x, fmt):
+    """128x1 runs down the columns (128 consecutive rows of one column) ->
+    (q [rows][cols], scale_inv [rows/128][cols])."""
+    x = _f32(x)
+    rows, cols = x.shape
+    assert rows % 128 == 0
+    t = x.reshape(rows // 128, 128, cols)
+    with np.errstate(invalid="ignore"):
+        a = np.abs(t).max(axis=1)  # [rows/128][cols], NaN-propagating
+    s, s_inv = recipe.current_scale(a, fmt)
+    q = scaled_encode(t, s[:, None, :], fmt).reshape(rows, cols)
+    return q, s_inv
+
+
+def cast_transpose_blockwise(x, fmt, granularity):
+    """(q, q_scale_inv, qT, qT_scale_inv) for granularity 1 (TILE_1x128) or 2 (BLOCK_128x128).
+
+    TILE_1x128: q in 1x128 runs along the columns (scale_inv [cols/128][rows]); qT = the
+    transposed codes of x quantised in 128x1 runs (scale_inv [rows/128][cols]).
+    BLOCK_128x128: q in 128x128 blocks; qT and its scale_inv are the transposes.
+    """
+    if granularity == 1:
+        q, q_sinv = quantize_tile_1x128(x, fmt)
+        qc, qt_sinv = quantize_tile_128x1(x, fmt)
+        return q, q_sinv, np.ascontiguousarray(qc.T), qt_sinv
+    if granularity == 2:
+        q, q_sinv = quantize_block_128x128(x, fmt)
+        return q, q_sinv, np.ascontiguousarray(q.T), np.ascontiguousarray(q_sinv.T)
+    raise ValueError("granularity")

@@ -31,8 +31,8 @@ FP8_SCALE_TENSOR, FP8_SCALE_TILE_1x128, FP8_SCALE_BLOCK_128x128, FP8_SCALE_MX_1x
 FP8_AMAX_ALGO_MAX = 0
 FP8_OK, FP8_ERR_ARG, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_DEVICE, FP8_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 
-EXPORTED = ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose", "fp8_gemm",
-            "fp8_last_error")
+EXPORTED = ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose",
+            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error")
 
 LIB_PATH = os.path.join(LIBDIR, LIBNAME)
 
@@ -53,9 +53,11 @@ def _load() -> ctypes.CDLL:
     lib.fp8_recipe_update.argtypes = [vp, vp, vp, ctypes.POINTER(i32), i32, i32, i32, i32, vp]
     lib.fp8_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_cast_transpose.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
+    lib.fp8_cast_transpose_blockwise.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_gemm.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
-    for name in ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose", "fp8_gemm"):
+    for name in ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose",
+                 "fp8_cast_transpose_blockwise", "fp8_gemm"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -163,6 +165,33 @@ def fp8_cast_transpose(x: torch.Tensor, fmt: int, scale: torch.Tensor, amax_slot
     _check(lib.fp8_cast_transpose(_ptr(x), _hp_dtype(x), rows, cols, fmt, _ptr(scale), _ptr(amax_slot), _ptr(q),
                                   _ptr(qT), _stream(x)))
     return q, qT
+
+
+def fp8_cast_transpose_blockwise(x: torch.Tensor, fmt: int, granularity: int, q: Optional[torch.Tensor] = None,
+                                 q_scale_inv: Optional[torch.Tensor] = None, qT: Optional[torch.Tensor] = None,
+                                 qT_scale_inv: Optional[torch.Tensor] = None):
+    """Current-scaling cast of x [rows][cols] and its transpose, each with its own scales ->
+    (q [rows][cols], q_scale_inv, qT [cols][rows], qT_scale_inv).  TILE_1x128: q_scale_inv
+    [cols/128][rows], qT_scale_inv [rows/128][cols]; BLOCK_128x128: [rows/128][cols/128] and
+    its transpose."""
+    _contig(x, "x")
+    rows, cols = _as2d(x)
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if qT is None:
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if granularity == FP8_SCALE_TILE_1x128:
+        qs, qts = (cols // 128, rows), (rows // 128, cols)
+    else:
+        qs, qts = (rows // 128, cols // 128), (cols // 128, rows // 128)
+    if q_scale_inv is None:
+        q_scale_inv = torch.empty(qs, dtype=torch.float32, device=dev)
+    if qT_scale_inv is None:
+        qT_scale_inv = torch.empty(qts, dtype=torch.float32, device=dev)
+    _check(lib.fp8_cast_transpose_blockwise(_ptr(x), _hp_dtype(x), rows, cols, fmt, granularity, _ptr(q),
+                                            _ptr(q_scale_inv), _ptr(qT), _ptr(qT_scale_inv), _stream(x)))
+    return q, q_scale_inv, qT, qT_scale_inv
 
 
 def fp8_gemm(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_a: int, B: torch.Tensor, fmt_b: int,

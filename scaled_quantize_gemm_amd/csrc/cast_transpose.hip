@@ -142,6 +142,170 @@ static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* sca
   return check_launch("fp8_cast_transpose");
 }
 
+// ------------------------------------------------------------------ blockwise cast-transpose
+//
+// The blockwise recipe's backward pass needs the transposed operands with their own scales
+// (DeepSeek-V3's blocks, per the course page's absmax bullet): for dgrad, W^T with the same
+// 128x128 blocks (transposed); for wgrad, X^T and dY^T with 1x128 runs along the new K (the
+// source's rows).  One 512-thread block per 128 x 128 source tile reads it once and writes
+// both copies:
+//   TILE:  q  uses one scale per source row run of 128 (scale_inv [cols/128][rows]),
+//          qT uses one scale per source column run of 128 (its rows; [rows/128][cols]);
+//   BLOCK: one scale for the tile in both (scale_inv [rows/128][cols/128] and, for qT, the
+//          transposed [cols/128][rows/128]).
+// Thread t holds source rows t/16 + 32p (p = 0..3), columns 8(t%16)..+8: row amaxes reduce
+// over 16 lanes, column amaxes over the wave's four 16-lane groups and then the 8 waves in
+// LDS.  The qT codes go through an LDS tile (dword pitch 33) and leave with 4x4 byte
+// transposes, 128 contiguous bytes of a qT row per 32 lanes.
+
+constexpr int kBwPitch = 33;
+
+template <int FMT, bool BF16, bool TILE>
+__global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __restrict__ x, int64_t rows,
+                                                                int64_t cols, uint8_t* __restrict__ q,
+                                                                float* __restrict__ q_sinv, uint8_t* __restrict__ qT,
+                                                                float* __restrict__ qT_sinv) {
+  __shared__ uint32_t lds[128 * kBwPitch];
+  __shared__ uint32_t cred[8][128];
+  __shared__ float cscale[128];
+  const int64_t nkb = cols >> 7, nrb = rows >> 7;
+  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r16 = t >> 4, cg = t & 15;
+  const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
+  float v[4][8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) load8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols, v[p]);
+  uint32_t m[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    m[p] = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = abs_bits(v[p][e]);
+      m[p] = m[p] > a ? m[p] : a;
+    }
+  }
+  float srow[4], scol[8];
+  if constexpr (TILE) {
+    // row runs: the 16 lanes sharing r16
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float si;
+      current_scale<FMT>(group_max_u32<16>(m[p]), srow[p], si);
+      if (cg == 0) q_sinv[kb * rows + rb * 128 + r16 + 32 * p] = si;  // [cols/128][rows]
+    }
+    // column runs: this thread's 4 rows, then the wave's 4 lane groups, then the 8 waves
+    uint32_t cm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a = abs_bits(v[p][e]);
+        c = c > a ? c : a;
+      }
+      uint32_t o = (uint32_t)__shfl_xor((int)c, 16, 64);
+      c = c > o ? c : o;
+      o = (uint32_t)__shfl_xor((int)c, 32, 64);
+      cm[e] = c > o ? c : o;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cred[wave][cg * 8 + e] = cm[e];
+    }
+    __syncthreads();
+    if (t < 128) {
+      uint32_t c = cred[0][t];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) c = c > cred[w][t] ? c : cred[w][t];
+      float sc, si;
+      current_scale<FMT>(c, sc, si);
+      cscale[t] = sc;
+      qT_sinv[rb * cols + kb * 128 + t] = si;  // [rows/128][cols]
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) scol[e] = cscale[cg * 8 + e];
+  } else {
+    uint32_t mx = m[0];
+#pragma unroll
+    for (int p = 1; p < 4; ++p) mx = mx > m[p] ? mx : m[p];
+    mx = wave_max_u32(mx);
+    if (lane == 0) cred[wave][0] = mx;
+    __syncthreads();
+    uint32_t bm = cred[0][0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) bm = bm > cred[w][0] ? bm : cred[w][0];
+    float sc, si;
+    current_scale<FMT>(bm, sc, si);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) srow[p] = sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) scol[e] = sc;
+    if (t == 0) {
+      q_sinv[rb * nkb + kb] = si;   // [rows/128][cols/128]
+      qT_sinv[kb * nrb + rb] = si;  // [cols/128][rows/128]
+    }
+  }
+  // q with the row scales; the qT codes (column scales) into the LDS tile
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float sr = srow[p];
+    uint32_t w0 = cvt4<FMT>(v[p][0] * sr, v[p][1] * sr, v[p][2] * sr, v[p][3] * sr);
+    uint32_t w1 = cvt4<FMT>(v[p][4] * sr, v[p][5] * sr, v[p][6] * sr, v[p][7] * sr);
+    uint32_t c0 = cvt4<FMT>(v[p][0] * scol[0], v[p][1] * scol[1], v[p][2] * scol[2], v[p][3] * scol[3]);
+    uint32_t c1 = cvt4<FMT>(v[p][4] * scol[4], v[p][5] * scol[5], v[p][6] * scol[6], v[p][7] * scol[7]);
+    if (m[p] > 0x7F800000u) {
+      w0 = patch_nan4(w0, &v[p][0]);
+      w1 = patch_nan4(w1, &v[p][4]);
+      c0 = patch_nan4(c0, &v[p][0]);
+      c1 = patch_nan4(c1, &v[p][4]);
+    }
+    const u32x2 w = {w0, w1};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(q + base + (int64_t)(r16 + 32 * p) * cols));
+    lds[(r16 + 32 * p) * kBwPitch + cg * 2] = c0;
+    lds[(r16 + 32 * p) * kBwPitch + cg * 2 + 1] = c1;
+  }
+  __syncthreads();
+  // transpose: 4 source rows x 4 source columns per dword quad
+  const int rg = t & 31, cgt = t >> 5;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cq = cgt + 16 * h;  // source columns 4cq .. 4cq+3
+    const uint32_t d0 = lds[(4 * rg + 0) * kBwPitch + cq];
+    const uint32_t d1 = lds[(4 * rg + 1) * kBwPitch + cq];
+    const uint32_t d2 = lds[(4 * rg + 2) * kBwPitch + cq];
+    const uint32_t d3 = lds[(4 * rg + 3) * kBwPitch + cq];
+    const uint32_t lo01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+    uint32_t o[4];
+    o[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_nontemporal_store(o[j],
+                                  reinterpret_cast<uint32_t*>(qT + (kb * 128 + 4 * cq + j) * rows + rb * 128 + 4 * rg));
+  }
+}
+
+template <int FMT, bool BF16>
+static int launch_ct_bw(const void* x, int64_t rows, int64_t cols, int gran, uint8_t* q, float* q_sinv, uint8_t* qT,
+                        float* qT_sinv, hipStream_t st) {
+  const int64_t blocks = (rows >> 7) * (cols >> 7);
+  if (gran == FP8_SCALE_TILE_1x128)
+    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, true>), dim3((unsigned)blocks), dim3(512), 0, st, x, rows,
+                       cols, q, q_sinv, qT, qT_sinv);
+  else
+    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, false>), dim3((unsigned)blocks), dim3(512), 0, st, x,
+                       rows, cols, q, q_sinv, qT, qT_sinv);
+  return check_launch("fp8_cast_transpose_blockwise");
+}
+
 }  // namespace sfp8
 
 using namespace sfp8;
@@ -166,4 +330,33 @@ extern "C" int fp8_cast_transpose(const void* x, int x_dtype, int64_t rows, int6
               : launch_ct<FP8_E4M3, false>(x, rows, cols, scale, amax_slot, q, qT, st);
   return bf ? launch_ct<FP8_E5M2, true>(x, rows, cols, scale, amax_slot, q, qT, st)
             : launch_ct<FP8_E5M2, false>(x, rows, cols, scale, amax_slot, q, qT, st);
+}
+
+extern "C" int fp8_cast_transpose_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int fmt,
+                                            int granularity, uint8_t* q, float* q_scale_inv, uint8_t* qT,
+                                            float* qT_scale_inv, void* stream) {
+  SFP8_REQUIRE(rows >= 0 && cols >= 0, FP8_ERR_SHAPE, "fp8_cast_transpose_blockwise: negative shape (%lld, %lld)",
+               (long long)rows, (long long)cols);
+  SFP8_REQUIRE(x_dtype == HP_F32 || x_dtype == HP_BF16, FP8_ERR_DTYPE, "fp8_cast_transpose_blockwise: x_dtype %d",
+               x_dtype);
+  SFP8_REQUIRE(fmt == FP8_E4M3 || fmt == FP8_E5M2, FP8_ERR_ARG, "fp8_cast_transpose_blockwise: fmt %d", fmt);
+  SFP8_REQUIRE(granularity == FP8_SCALE_TILE_1x128 || granularity == FP8_SCALE_BLOCK_128x128, FP8_ERR_ARG,
+               "fp8_cast_transpose_blockwise: granularity %d (TILE_1x128 or BLOCK_128x128)", granularity);
+  SFP8_REQUIRE(rows % 128 == 0 && cols % 128 == 0, FP8_ERR_SHAPE,
+               "fp8_cast_transpose_blockwise: rows=%lld and cols=%lld must be multiples of 128", (long long)rows,
+               (long long)cols);
+  if (rows * cols == 0) return FP8_OK;
+  SFP8_REQUIRE(x != nullptr && q != nullptr && qT != nullptr && q_scale_inv != nullptr && qT_scale_inv != nullptr,
+               FP8_ERR_ARG, "fp8_cast_transpose_blockwise: null pointer");
+  SFP8_REQUIRE(aligned16(x) && aligned16(q) && aligned16(qT), FP8_ERR_ARG,
+               "fp8_cast_transpose_blockwise: x, q and qT must be 16-byte aligned");
+  SFP8_REQUIRE(aligned4(q_scale_inv) && aligned4(qT_scale_inv), FP8_ERR_ARG,
+               "fp8_cast_transpose_blockwise: scale_inv arrays must be 4-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = x_dtype == HP_BF16;
+  if (fmt == FP8_E4M3)
+    return bf ? launch_ct_bw<FP8_E4M3, true>(x, rows, cols, granularity, q, q_scale_inv, qT, qT_scale_inv, st)
+              : launch_ct_bw<FP8_E4M3, false>(x, rows, cols, granularity, q, q_scale_inv, qT, qT_scale_inv, st);
+  return bf ? launch_ct_bw<FP8_E5M2, true>(x, rows, cols, granularity, q, q_scale_inv, qT, qT_scale_inv, st)
+            : launch_ct_bw<FP8_E5M2, false>(x, rows, cols, granularity, q, q_scale_inv, qT, qT_scale_inv, st);
 }

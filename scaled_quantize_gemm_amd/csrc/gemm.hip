@@ -20,6 +20,7 @@
 // Scaling modes:
 //  * TENSOR:  acc over all K; C = acc * (sa * sb).
 //  * BLOCK:   per 128-K block kb: p = MFMA from zero; acc += p * (sa[kb][m] * sb[n/128][kb]).
+//  * TILE2:   both operands in 1x128 runs along K: acc += p * (sa[kb][m] * sb[kb][n]).
 //  * MX:      scaled MFMA with the e8m0 codes of A[m][4kb+g] and B[n][4kb+g]; C = acc.
 #include <type_traits>
 
@@ -30,7 +31,7 @@ namespace sfp8 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-enum { MODE_TENSOR = 0, MODE_BLOCK = 1, MODE_MX = 2 };
+enum { MODE_TENSOR = 0, MODE_BLOCK = 1, MODE_MX = 2, MODE_TILE2 = 3 };
 
 template <int BM, int BN>
 struct GemmCfg {
@@ -110,12 +111,20 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
     if (ks + 1 < nk) load_step(ks + 1);
 
     // ---- per-step scale operands
-    float sab[Cfg::TM][4];
+    float sab[Cfg::TM][4], sbc[Cfg::TN];
     int scale_a[Cfg::TM], scale_b[Cfg::TN];
-    if constexpr (MODE == MODE_BLOCK) {
+    if constexpr (MODE == MODE_BLOCK || MODE == MODE_TILE2) {
       const float* sa = static_cast<const float*>(sa_p);
       const float* sb = static_cast<const float*>(sb_p);
-      const float sbv = sb[(size_t)(n0 / 128) * nk + ks];
+      const float sbv = MODE == MODE_BLOCK ? sb[(size_t)(n0 / 128) * nk + ks] : 1.0f;
+      if constexpr (MODE == MODE_TILE2) {
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j) {
+          int gn = n0 + wn * Cfg::WN + 16 * j + r;
+          gn = gn < N ? gn : N - 1;
+          sbc[j] = sb[(size_t)ks * N + gn];  // [K/128][N]
+        }
+      }
 #pragma unroll
       for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
@@ -175,7 +184,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
           v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], v4f{0.f, 0.f, 0.f, 0.f}, FA, FB, 0,
                                                                     0, 0, 0);
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = fmaf(p[jj], sab[i][jj], acc[i][j][jj]);
+          for (int jj = 0; jj < 4; ++jj)
+            acc[i][j][jj] = fmaf(p[jj], MODE == MODE_TILE2 ? sab[i][jj] * sbc[j] : sab[i][jj], acc[i][j][jj]);
         }
       }
 
@@ -633,7 +643,9 @@ __device__ __forceinline__ int blk_row_of(int q) { return (q & ~63) + 4 * (q & 1
 // position of 16-byte chunk c in 128-byte LDS row q (the small-tile kernel's swizzle)
 __device__ __forceinline__ int blk_pos(int q, int c) { return c ^ (((q >> 1) ^ ((q & 1) << 2)) & 7); }
 
-template <int FA, int FB, int OUT>
+// MODE: MODE_BLOCK (B scales per 128x128 block: one value per stage) or MODE_TILE2 (B scales
+// per 1x128 run along K: one per column per stage, [K/128][N])
+template <int MODE, int FA, int FB, int OUT>
 __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                           const float* __restrict__ sa_p,
                                                           const float* __restrict__ sb_p, void* __restrict__ C, int M,
@@ -679,14 +691,21 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
                                            (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
     const int row = wave * 64 + lane;
     s_voff = (uint32_t)(row < lim_a ? row : lim_a - 1) * 4;
-  } else {
+  } else if constexpr (MODE == MODE_BLOCK) {
     const uint64_t bytes = ((uint64_t)tiles_n * nkb - (uint64_t)tn * nkb) * 4;
     rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb_p + (size_t)tn * nkb), (short)0,
                                            (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
     s_voff = 0;
+  } else {
+    // waves 4 and 5 load the tile's 128 column scales; 6 and 7 repeat them into unused slots
+    const uint64_t bytes = ((uint64_t)nkb * N - n0) * 4;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb_p + n0), (short)0,
+                                           (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
+    const int col = (wave & 1) * 64 + lane;
+    s_voff = (uint32_t)(col < lim_b ? col : lim_b - 1) * 4;
   }
   const int s_lds = s_is_a ? BLK_SA_OFF + wave * 256 : BLK_SB_OFF + (wave - 4) * 256;
-  const uint32_t s_step = s_is_a ? (uint32_t)M * 4 : 4;
+  const uint32_t s_step = s_is_a ? (uint32_t)M * 4 : (MODE == MODE_BLOCK ? 4u : (uint32_t)N * 4);
   auto issue = [&](int ks, int st) {
     uint8_t* buf = smem + st * STAGE;
 #pragma unroll
@@ -714,7 +733,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     b_lo[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g) << 4);
     b_hi[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g + 4) << 4);
     s_a[st] = base + BLK_SA_OFF + (slab_a + 16 * g) * 4;
-    s_b[st] = base + BLK_SB_OFF;
+    s_b[st] = base + BLK_SB_OFF + (MODE == MODE_TILE2 ? (slab_b + 4 * r) * 4 : 0);
   }
 
   v4f acc[4][4];
@@ -723,7 +742,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i fa[4], fb[4];
-  float fsa[16], fsb = 0.f;
+  float fsa[16], fsb[4] = {0.f, 0.f, 0.f, 0.f};
   auto pack = [](const u32x4& lo, const u32x4& hi) -> v8i {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
@@ -749,20 +768,30 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       fsa[4 * h + 2] = __uint_as_float(sv[h].z);
       fsa[4 * h + 3] = __uint_as_float(sv[h].w);
     }
-    fsb = __uint_as_float(ds_read4<0>(s_b[ST]));
+    if constexpr (MODE == MODE_BLOCK) {
+      fsb[0] = __uint_as_float(ds_read4<0>(s_b[ST]));
+    } else {
+      const u32x4 sbv = ds_read16<0>(s_b[ST]);  // columns 4r .. 4r+3 of the slab
+      fsb[0] = __uint_as_float(sbv.x);
+      fsb[1] = __uint_as_float(sbv.y);
+      fsb[2] = __uint_as_float(sbv.z);
+      fsb[3] = __uint_as_float(sbv.w);
+    }
   };
   // 16 MFMAs, each partial folded into its accumulators two MFMAs later:
-  // acc[i][j][jj] += p * (sa[row 16g + 4jj + i] * sb)
+  // acc[i][j][jj] += p * (sa[row 16g + 4jj + i] * sb[block] or sb[column 4r + j])
   auto compute = [&]() {
     float sab[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sab[e] = fsa[e] * fsb;
+    for (int e = 0; e < 16; ++e) sab[e] = MODE == MODE_BLOCK ? fsa[e] * fsb[0] : fsa[e];
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     v4f p[16];
     auto fold = [&](int t) {
       const int i = t >> 2, j = t & 3;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = fmaf(p[t][jj], sab[4 * jj + i], acc[i][j][jj]);
+      for (int jj = 0; jj < 4; ++jj)
+        acc[i][j][jj] =
+            fmaf(p[t][jj], MODE == MODE_BLOCK ? sab[4 * jj + i] : sab[4 * jj + i] * fsb[j], acc[i][j][jj]);
     };
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -862,7 +891,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 template <int MODE, int FA, int FB, int OUT>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, void* C, int M, int N, int K,
                        hipStream_t st) {
-  if constexpr (MODE != MODE_BLOCK) {
+  if constexpr (MODE == MODE_TENSOR || MODE == MODE_MX) {
     const int tiles_m = (M + BIG_BM - 1) / BIG_BM, tiles_n = (N + BIG_BN - 1) / BIG_BN;
     // large problems only (>= half a wave of tiles on 256 CUs); MX scale rows are read as
     // 4-byte runs, so M and N must be multiples of 4 there
@@ -879,12 +908,13 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
       }
     }
   }
-  if constexpr (MODE == MODE_BLOCK) {
+  if constexpr (MODE == MODE_BLOCK || MODE == MODE_TILE2) {
     const int tiles_m = (M + BLK_BM - 1) / BLK_BM, tiles_n = (N + BLK_BN - 1) / BLK_BN;
     // large problems only; 32-bit offsets for a tile's rows and a stage's scales
-    const bool offsets32 = 256ll * K < (1ll << 32) && (int64_t)(K / 128) * M * 4 < (1ll << 32);
+    const int64_t mn = M > N ? M : N;
+    const bool offsets32 = 256ll * K < (1ll << 32) && (int64_t)(K / 128) * mn * 4 < (1ll << 32);
     if (tiles_m * tiles_n >= 128 && offsets32) {
-      hipLaunchKernelGGL((gemm_blk_kernel<FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
                          static_cast<const float*>(sa), static_cast<const float*>(sb), C, M, N, K, tiles_m, tiles_n);
       return check_launch("fp8_gemm");
     }
@@ -931,11 +961,12 @@ extern "C" int fp8_gemm(const uint8_t* A, int fmt_a, const void* a_scale_inv, in
   int mode;
   if (gran_a == FP8_SCALE_TENSOR && gran_b == FP8_SCALE_TENSOR) mode = MODE_TENSOR;
   else if (gran_a == FP8_SCALE_TILE_1x128 && gran_b == FP8_SCALE_BLOCK_128x128) mode = MODE_BLOCK;
+  else if (gran_a == FP8_SCALE_TILE_1x128 && gran_b == FP8_SCALE_TILE_1x128) mode = MODE_TILE2;
   else if (gran_a == FP8_SCALE_MX_1x32 && gran_b == FP8_SCALE_MX_1x32) mode = MODE_MX;
   else
     return set_error(FP8_ERR_ARG,
-                     "fp8_gemm: granularity pair (%d, %d) unsupported; use TENSORxTENSOR, TILE_1x128xBLOCK_128x128 or "
-                     "MX_1x32xMX_1x32",
+                     "fp8_gemm: granularity pair (%d, %d) unsupported; use TENSORxTENSOR, TILE_1x128xBLOCK_128x128, "
+                     "TILE_1x128xTILE_1x128 or MX_1x32xMX_1x32",
                      gran_a, gran_b);
   if (M == 0 || N == 0) return FP8_OK;
   SFP8_REQUIRE(C != nullptr && a_scale_inv != nullptr && b_scale_inv != nullptr, FP8_ERR_ARG,
@@ -951,5 +982,7 @@ extern "C" int fp8_gemm(const uint8_t* A, int fmt_a, const void* a_scale_inv, in
     return dispatch_fmt<MODE_TENSOR>(fmt_a, fmt_b, c_dtype, A, B, a_scale_inv, b_scale_inv, C, m, n, k, st);
   if (mode == MODE_BLOCK)
     return dispatch_fmt<MODE_BLOCK>(fmt_a, fmt_b, c_dtype, A, B, a_scale_inv, b_scale_inv, C, m, n, k, st);
+  if (mode == MODE_TILE2)
+    return dispatch_fmt<MODE_TILE2>(fmt_a, fmt_b, c_dtype, A, B, a_scale_inv, b_scale_inv, C, m, n, k, st);
   return dispatch_fmt<MODE_MX>(fmt_a, fmt_b, c_dtype, A, B, a_scale_inv, b_scale_inv, C, m, n, k, st);
 }

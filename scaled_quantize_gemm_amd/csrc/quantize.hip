@@ -196,66 +196,58 @@ __global__ void __launch_bounds__(256) quant_tile_kernel(const void* __restrict_
 
 // ------------------------------------------------------------------ 128x128 blocks
 //
-// One 1024-thread block per 128 x 512 region (four 128x128 scale blocks side by side): wave w
-// takes rows 8w..8w+7, and on each row its 64 lanes read 512 consecutive elements (16 lanes
-// per scale block), so every load instruction reads 1 KB of bf16 contiguous.  The values stay
-// in registers through the reduction (16-lane shuffles, then across the 16 waves in LDS).
-// Consecutive blocks walk the input in address order.  A partial last row block uses the
-// rows present (absent rows contribute nothing).
+// One 512-thread block per 128x128 block (blocks in address order): thread t covers rows
+// t/16 + 32p (p = 0..3), columns 8(t%16)..+8, so each load instruction reads 4 whole
+// 256-byte block rows; the 32 values stay in registers through the block reduction (wave
+// shuffles, then the 8 waves in LDS).  A partial last row block uses the rows present
+// (absent rows contribute nothing).
 
-constexpr int kBlockThreads = 1024;
-constexpr int kBlockRowsPerWave = 8;
+constexpr int kBlockThreads = 512;
 
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(kBlockThreads) quant_block_kernel(const void* __restrict__ x, int64_t rows,
                                                                    int64_t cols, uint8_t* __restrict__ q,
                                                                    float* __restrict__ sinv_out) {
-  __shared__ uint32_t red[16][4];
+  __shared__ uint32_t red[8];
   const int64_t nkb = cols >> 7;
-  const int64_t ncb = (nkb + 3) >> 2;
-  const int64_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int grp = lane >> 4;  // scale block within the region
-  const int64_t kb = cb * 4 + grp;
-  const int64_t row0 = rb * 128 + wave * kBlockRowsPerWave;
-  const int64_t c0 = kb * 128 + (lane & 15) * 8;
-  const bool col_ok = kb < nkb;  // whole 16-lane groups
-  float v[kBlockRowsPerWave][8];
-  uint32_t m[kBlockRowsPerWave], mx = 0;
+  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
+  const int t = threadIdx.x, r16 = t >> 4, cg = t & 15;
+  const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
+  float v[4][8];
+  uint32_t m[4], mx = 0;
 #pragma unroll
-  for (int j = 0; j < kBlockRowsPerWave; ++j) {
-    if (col_ok && row0 + j < rows) {
-      load8<BF16>(x, (row0 + j) * cols + c0, v[j]);
+  for (int p = 0; p < 4; ++p) {
+    if (rb * 128 + r16 + 32 * p < rows) {
+      load8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols, v[p]);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
+      for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
     }
   }
 #pragma unroll
-  for (int j = 0; j < kBlockRowsPerWave; ++j) {
-    m[j] = 0;
+  for (int p = 0; p < 4; ++p) {
+    m[p] = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t a = abs_bits(v[j][i]);
-      m[j] = m[j] > a ? m[j] : a;
+      const uint32_t a = abs_bits(v[p][i]);
+      m[p] = m[p] > a ? m[p] : a;
     }
-    mx = mx > m[j] ? mx : m[j];
+    mx = mx > m[p] ? mx : m[p];
   }
-  mx = group_max_u32<16>(mx);
-  if ((lane & 15) == 0) red[wave][grp] = mx;
+  mx = wave_max_u32(mx);
+  if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
-  uint32_t bm = red[0][grp];
+  uint32_t bm = red[0];
 #pragma unroll
-  for (int w = 1; w < 16; ++w) bm = bm > red[w][grp] ? bm : red[w][grp];
+  for (int i = 1; i < 8; ++i) bm = bm > red[i] ? bm : red[i];
   float s, s_inv;
   current_scale<FMT>(bm, s, s_inv);
-  if (col_ok) {
 #pragma unroll
-    for (int j = 0; j < kBlockRowsPerWave; ++j)
-      if (row0 + j < rows)
-        __builtin_nontemporal_store(cast8<FMT>(v[j], s, m[j]), reinterpret_cast<u32x2*>(q + (row0 + j) * cols + c0));
-    if (wave == 0 && (lane & 15) == 0) sinv_out[rb * nkb + kb] = s_inv;
-  }
+  for (int p = 0; p < 4; ++p)
+    if (rb * 128 + r16 + 32 * p < rows)
+      __builtin_nontemporal_store(cast8<FMT>(v[p], s, m[p]),
+                                  reinterpret_cast<u32x2*>(q + base + (int64_t)(r16 + 32 * p) * cols));
+  if (t == 0) sinv_out[rb * nkb + kb] = s_inv;
 }
 
 // ------------------------------------------------------------------ MX 1x32
@@ -368,7 +360,7 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
     hipLaunchKernelGGL((quant_tile_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
                        static_cast<float*>(sinv));
   } else if (gran == FP8_SCALE_BLOCK_128x128) {
-    const int64_t blocks = ((rows + 127) / 128) * (((cols >> 7) + 3) / 4);
+    const int64_t blocks = ((rows + 127) / 128) * (cols >> 7);
     hipLaunchKernelGGL((quant_block_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, x, rows,
                        cols, q, static_cast<float*>(sinv));
   } else {

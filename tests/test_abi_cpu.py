@@ -20,7 +20,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose",
-                            "fp8_gemm", "fp8_last_error"])
+                            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -83,11 +83,21 @@ def test_argument_errors_return_before_launch():
     assert lib.fp8_cast_transpose(fake, 1, 4, 4, 0, None, None, fake, fake, None) == sq.FP8_ERR_ARG
     assert lib.fp8_cast_transpose(fake, 2, 4, 4, 0, fake, None, fake, fake, None) == sq.FP8_ERR_DTYPE
     assert lib.fp8_cast_transpose(None, 1, 0, 5, 0, fake, None, None, None, None) == sq.FP8_OK
+    # blockwise cast-transpose: granularity, shapes that are not multiples of 128, dtype, empty
+    ct = lib.fp8_cast_transpose_blockwise
+    assert ct(fake, 1, 128, 128, 0, 0, fake, fake, fake, fake, None) == sq.FP8_ERR_ARG
+    assert ct(fake, 1, 128, 128, 0, 3, fake, fake, fake, fake, None) == sq.FP8_ERR_ARG
+    assert ct(fake, 1, 100, 128, 0, 1, fake, fake, fake, fake, None) == sq.FP8_ERR_SHAPE
+    assert ct(fake, 1, 128, 200, 0, 2, fake, fake, fake, fake, None) == sq.FP8_ERR_SHAPE
+    assert ct(fake, 5, 128, 128, 0, 1, fake, fake, fake, fake, None) == sq.FP8_ERR_DTYPE
+    assert ct(fake, 1, 128, 128, 0, 1, fake, None, fake, fake, None) == sq.FP8_ERR_ARG
+    assert ct(None, 1, 0, 128, 0, 2, None, None, None, None, None) == sq.FP8_OK
     # gemm: K not a multiple of 128, bad pair, bad out dtype, empty
     assert lib.fp8_gemm(fake, 0, fake, 0, fake, 0, fake, 0, fake, 0, 4, 4, 100, None) == sq.FP8_ERR_SHAPE
     assert lib.fp8_gemm(fake, 0, fake, 0, fake, 0, fake, 3, fake, 0, 4, 4, 128, None) == sq.FP8_ERR_ARG
     assert "granularity" in sq.fp8_last_error()
-    assert lib.fp8_gemm(fake, 0, fake, 1, fake, 0, fake, 1, fake, 0, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert lib.fp8_gemm(fake, 0, fake, 2, fake, 0, fake, 1, fake, 0, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert lib.fp8_gemm(fake, 0, fake, 1, fake, 0, fake, 3, fake, 0, 4, 4, 128, None) == sq.FP8_ERR_ARG
     assert lib.fp8_gemm(fake, 0, fake, 0, fake, 0, fake, 0, fake, 7, 4, 4, 128, None) == sq.FP8_ERR_DTYPE
     assert lib.fp8_gemm(fake, 0, fake, 0, fake, 0, fake, 0, fake, 0, 0, 4, 128, None) == sq.FP8_OK
     assert lib.fp8_gemm(fake, 2, fake, 0, fake, 0, fake, 0, fake, 0, 4, 4, 128, None) == sq.FP8_ERR_ARG

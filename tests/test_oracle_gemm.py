@@ -154,7 +154,7 @@ def test_gemm_closed_forms():
     assert np.all(C == 256.0) and np.all(S == 256.0)
 
 
-@pytest.mark.parametrize("mode", ["tensor", "blockwise", "mx"])
+@pytest.mark.parametrize("mode", ["tensor", "blockwise", "tile2", "mx"])
 def test_gemm_brute_force_fractions(mode):
     rng = np.random.default_rng(11)
     M, N, K = 3, 5, 256
@@ -170,6 +170,12 @@ def test_gemm_brute_force_fractions(mode):
         ga, gb = gemm.TILE_1x128, gemm.BLOCK_128x128
         fa_ = lambda m, k: Fraction(float(sa[k // 128, m]))
         fb_ = lambda n, k: Fraction(float(sb[n // 128, k // 128]))
+    elif mode == "tile2":
+        sa = rng.uniform(0.1, 3, (K // 128, M)).astype(np.float32)
+        sb = rng.uniform(0.1, 3, (K // 128, N)).astype(np.float32)
+        ga, gb = gemm.TILE_1x128, gemm.TILE_1x128
+        fa_ = lambda m, k: Fraction(float(sa[k // 128, m]))
+        fb_ = lambda n, k: Fraction(float(sb[k // 128, n]))
     else:
         sa = rng.integers(100, 150, (M, K // 32)).astype(np.uint8)
         sb = rng.integers(100, 150, (N, K // 32)).astype(np.uint8)

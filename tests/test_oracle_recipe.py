@@ -209,3 +209,64 @@ def test_mx_zero_and_nan_groups():
     q, codes = quantize.quantize_mx_1x32(x, E4M3)
     assert codes[0, 0] == 0 and codes[0, 1] == 255
     assert q[0, 40] == 0x7F and np.all(q[0, :32] == 0)
+
+
+# --------------------------------------------------------------------------- blockwise transposes
+
+
+def _bw_data(seed, rows=256, cols=384):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-8, 8, (1, cols))).astype(np.float32)  # column-dependent magnitudes
+    return x
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_column_runs_max_hits_fmax(fmt):
+    """Every non-zero 128x1 run of the transposed copy holds a code of magnitude fmax (its
+    amax element), and its scale is fmax / that run's amax."""
+    x = _bw_data(21)
+    x[128:256, 5] = 0.0  # a zero run: unit scale
+    _, _, qT, sT = quantize.cast_transpose_blockwise(x, fmt, 1)
+    fmax_code = 0x7E if fmt == E4M3 else 0x7B
+    for c in range(x.shape[1]):
+        for rb in range(2):
+            run = qT[c, rb * 128:(rb + 1) * 128]
+            a = np.abs(x[rb * 128:(rb + 1) * 128, c]).max()
+            if a == 0:
+                assert sT[rb, c] == 1.0 and np.all((run & 0x7F) == 0)
+            else:
+                assert np.any((run & 0x7F) == fmax_code)
+                assert sT[rb, c] == f32(1) / (f32(fp8.FMAX[fmt]) / f32(a))
+
+
+def test_column_runs_outlier_spoils_only_its_run():
+    """An outlier changes the codes of its own 128x1 run in the transposed copy and of its own
+    1x128 run in the forward copy, and nothing else."""
+    x = _bw_data(22)
+    y = x.copy()
+    y[200, 7] *= 1000.0
+    q0, _, t0, _ = quantize.cast_transpose_blockwise(x, E4M3, 1)
+    q1, _, t1, _ = quantize.cast_transpose_blockwise(y, E4M3, 1)
+    dq = np.argwhere(q0 != q1)
+    assert len(dq) and np.all(dq[:, 0] == 200) and np.all(dq[:, 1] // 128 == 0)
+    dt = np.argwhere(t0 != t1)
+    assert len(dt) and np.all(dt[:, 0] == 7) and np.all(dt[:, 1] // 128 == 1)
+
+
+def test_column_runs_brute_force():
+    x = _bw_data(23, rows=128, cols=128)
+    _, _, qT, sT = quantize.cast_transpose_blockwise(x, E4M3, 1)
+    for c in range(0, 128, 13):
+        a = np.abs(x[:, c]).max()
+        s = f32(448.0) / f32(a)
+        for r in range(0, 128, 11):
+            assert qT[c, r] == fp8.encode_scalar(float(f32(x[r, c] * s)), E4M3)
+
+
+def test_block_transpose_is_transpose_of_codes_and_scales():
+    x = _bw_data(24)
+    q, s, qT, sT = quantize.cast_transpose_blockwise(x, E4M3, 2)
+    q2, s2 = quantize.quantize_block_128x128(x.T, E4M3)  # the same blocks, seen transposed
+    assert np.array_equal(qT, q.T) and np.array_equal(sT, s.T)
+    assert np.array_equal(qT, q2) and np.array_equal(sT, s2)

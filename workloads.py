@@ -22,7 +22,8 @@ Workloads
    ~N(0,1e-3); X and dY fresh each step, W fixed.
 3  blockwise current scaling, bf16: X [4096x7168] ~N(0,1) with 0.1% of the
    entries (uniform positions, no repeats) multiplied by 100 before the bf16
-   conversion; W [7168x7168] ~N(0,0.02).
+   conversion; W [7168x7168] ~N(0,0.02); for the blockwise backward, the
+   output gradient dY [4096x7168] ~N(0,1e-3).
 4  large SwiGLU FC1, bf16: X [8192x4096] ~N(0,1), W [14336x4096] ~N(0,0.02),
    dY [8192x14336] ~N(0,1e-4).
 5  MX square GEMM, bf16: A, B [8192x8192] ~N(0,1); plus a standalone
@@ -93,6 +94,11 @@ def w3_inputs(seed: int = 0, m: int = 4096, k: int = 7168, n: int = 7168):
     x = with_outliers(x, 0.001, 100.0, seed, 301).to(torch.bfloat16)
     w = normal((n, k), 0.02, seed, 302, torch.bfloat16)
     return x, w
+
+
+def w3_grad(seed: int = 0, m: int = 4096, n: int = 7168):
+    """Output gradient dY [m][n] for the blockwise backward."""
+    return normal((m, n), 1e-3, seed, 303, torch.bfloat16)
 
 
 # --------------------------------------------------------------------------- workload 4
