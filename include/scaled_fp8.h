@@ -139,6 +139,23 @@ int fp8_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int fmt
                  void *scale_inv_out, void *stream);
 
 /*
+ * fp8_quantize_diag -- fp8_quantize(FP8_SCALE_TENSOR) plus cast diagnostics in the same pass.
+ *   [L] Diagnostic playbook (FP8 loss spikes or NaN: inspect per-layer amax and overflow
+ *   counts) and Worked example 02 (with a stale delayed scale, a spike clips at 448).
+ *
+ *   Same arguments, element rule and amax as fp8_quantize with FP8_SCALE_TENSOR, plus
+ *   counts     device uint64 [3], 8-byte aligned; the call ADDS (the caller zeroes them):
+ *                counts[0]  saturated:   elements with |fp32(x * s)| > fmax (the code was
+ *                                        clipped to +-fmax; +-inf inputs included)
+ *                counts[1]  underflowed: finite non-zero elements whose code is +-0
+ *                counts[2]  nan:         NaN elements
+ *   Errors: as fp8_quantize; FP8_ERR_ARG also for a null or misaligned counts.
+ */
+int fp8_quantize_diag(const void *x, int x_dtype, int64_t rows, int64_t cols, int fmt,
+                      const float *scale, float *amax_slot, uint8_t *q,
+                      unsigned long long *counts, void *stream);
+
+/*
  * fp8_cast_transpose -- per-tensor cast plus its transpose in one pass (+ amax).
  *   The backward pass of the hybrid recipe ([L] Part 01: E4M3 forward, E5M2 gradients;
  *   [W] FP8 bullet) multiplies by transposed operands; producing the transposed FP8 copy

@@ -135,3 +135,17 @@ def cast_transpose_blockwise(x, fmt, granularity):
         q, q_sinv = quantize_block_128x128(x, fmt)
         return q, q_sinv, np.ascontiguousarray(q.T), np.ascontiguousarray(q_sinv.T)
     raise ValueError("granularity")
+
+
+def cast_diagnostics(x, scale, fmt):
+    """(saturated, underflowed, nan) element counts of the per-tensor cast with ``scale``:
+    saturated = |fp32(x * s)| > fmax (the code is clipped), underflowed = x finite and
+    non-zero whose code decodes to 0, nan = NaN inputs."""
+    x = _f32(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (x * np.float32(scale)).astype(np.float32)
+        saturated = int(np.count_nonzero(np.abs(y) > fp8.FMAX[fmt]))
+    q = fp8.encode(y, fmt)
+    finite_nz = np.isfinite(x) & (x != 0)
+    underflowed = int(np.count_nonzero(finite_nz & (fp8.decode(q, fmt) == 0)))
+    return saturated, underflowed, int(np.count_nonzero(np.isnan(x)))

@@ -31,7 +31,7 @@ FP8_SCALE_TENSOR, FP8_SCALE_TILE_1x128, FP8_SCALE_BLOCK_128x128, FP8_SCALE_MX_1x
 FP8_AMAX_ALGO_MAX = 0
 FP8_OK, FP8_ERR_ARG, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_DEVICE, FP8_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 
-EXPORTED = ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose",
+EXPORTED = ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag", "fp8_cast_transpose",
             "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error")
 
 LIB_PATH = os.path.join(LIBDIR, LIBNAME)
@@ -52,11 +52,12 @@ def _load() -> ctypes.CDLL:
     lib.fp8_device_check.argtypes = [i32, ctypes.c_char_p, sz]
     lib.fp8_recipe_update.argtypes = [vp, vp, vp, ctypes.POINTER(i32), i32, i32, i32, i32, vp]
     lib.fp8_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.fp8_quantize_diag.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.fp8_cast_transpose.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.fp8_cast_transpose_blockwise.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_gemm.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
-    for name in ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose",
+    for name in ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag", "fp8_cast_transpose",
                  "fp8_cast_transpose_blockwise", "fp8_gemm"):
         getattr(lib, name).restype = i32
     return lib
@@ -151,6 +152,21 @@ def fp8_quantize(x: torch.Tensor, fmt: int, granularity: int = FP8_SCALE_TENSOR,
     _check(lib.fp8_quantize(_ptr(x), _hp_dtype(x), rows, cols, fmt, granularity, _ptr(scale), _ptr(amax_slot),
                             _ptr(q), _ptr(scale_inv_out), _stream(x)))
     return q, scale_inv_out
+
+
+def fp8_quantize_diag(x: torch.Tensor, fmt: int, scale: torch.Tensor, counts: torch.Tensor,
+                      amax_slot: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-tensor cast with diagnostics: adds (saturated, underflowed, nan) element counts to
+    `counts` (device int64 [3]); returns q."""
+    _contig(x, "x")
+    rows, cols = _as2d(x)
+    if counts.dtype != torch.int64 or counts.numel() != 3:
+        raise TypeError("counts must be a device int64 tensor of 3 entries")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    _check(lib.fp8_quantize_diag(_ptr(x), _hp_dtype(x), rows, cols, fmt, _ptr(scale), _ptr(amax_slot), _ptr(q),
+                                 _ptr(counts), _stream(x)))
+    return q
 
 
 def fp8_cast_transpose(x: torch.Tensor, fmt: int, scale: torch.Tensor, amax_slot: Optional[torch.Tensor] = None,

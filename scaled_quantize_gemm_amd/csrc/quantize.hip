@@ -86,12 +86,31 @@ __device__ __forceinline__ u32x2 cast8(const float (&v)[8], float s, uint32_t am
   return u32x2{w0, w1};
 }
 
-template <int FMT, bool BF16>
+// Cast diagnostics (DIAG): per element, saturated = |fp32(x s)| > fmax (so the code was
+// clipped), underflowed = x finite and non-zero but its code is +-0, nan = x is NaN; block
+// sums are added to counts[0..2] with one 64-bit atomic each.
+template <int FMT>
+__device__ __forceinline__ void diag8(const float (&v)[8], float s, u32x2 codes, uint32_t (&cnt)[3]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = v[i] * s;
+    const uint32_t a = abs_bits(v[i]);
+    const uint32_t code = ((i < 4 ? codes.x : codes.y) >> (8 * (i & 3))) & 0x7Fu;
+    cnt[0] += fabsf(y) > Fp8Traits<FMT>::fmax ? 1u : 0u;
+    cnt[1] += (a != 0 && a < 0x7F800000u && code == 0) ? 1u : 0u;
+    cnt[2] += a > 0x7F800000u ? 1u : 0u;
+  }
+}
+
+template <int FMT, bool BF16, bool DIAG>
 __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void* __restrict__ x, int64_t n,
                                                                       const float* __restrict__ scale_p,
                                                                       uint32_t* __restrict__ amax_slot,
-                                                                      uint8_t* __restrict__ q) {
+                                                                      uint8_t* __restrict__ q,
+                                                                      unsigned long long* __restrict__ counts) {
   __shared__ uint32_t red[4];
+  __shared__ uint32_t cred[DIAG ? 3 : 1][4];
+  uint32_t cnt[3] = {0, 0, 0};
   const float s = *scale_p;
   const int64_t npieces = n >> 3;
   const int64_t step = (int64_t)gridDim.x * kTensorThreads * kTensorPieces;
@@ -113,8 +132,10 @@ __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void
           const uint32_t a = abs_bits(v[j][i]);
           m = m > a ? m : a;
         }
-        __builtin_nontemporal_store(cast8<FMT>(v[j], s, m), reinterpret_cast<u32x2*>(q + (pc << 3)));
+        const u32x2 codes = cast8<FMT>(v[j], s, m);
+        __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + (pc << 3)));
         mxf = mxf > m ? mxf : m;
+        if constexpr (DIAG) diag8<FMT>(v[j], s, codes, cnt);
       }
     }
   }
@@ -122,11 +143,32 @@ __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
     const int64_t i = (npieces << 3) + threadIdx.x;
     float xv = load_one<BF16>(x, i);
-    q[i] = cast_one<FMT>(xv, s);
+    const uint8_t c = cast_one<FMT>(xv, s);
+    q[i] = c;
     uint32_t a = abs_bits(xv);
     mxf = mxf > a ? mxf : a;
+    if constexpr (DIAG) {
+      cnt[0] += fabsf(xv * s) > Fp8Traits<FMT>::fmax ? 1u : 0u;
+      cnt[1] += (a != 0 && a < 0x7F800000u && (c & 0x7Fu) == 0) ? 1u : 0u;
+      cnt[2] += a > 0x7F800000u ? 1u : 0u;
+    }
   }
-  uint32_t r = block_max_u32_256(mxf, red);
+  if constexpr (DIAG) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      uint32_t v = cnt[k];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
+      if ((threadIdx.x & 63) == 0) cred[k][threadIdx.x >> 6] = v;
+    }
+  }
+  uint32_t r = block_max_u32_256(mxf, red);  // (its barrier also publishes cred)
+  if constexpr (DIAG) {
+    if (threadIdx.x < 3) {
+      const uint32_t tot = cred[threadIdx.x][0] + cred[threadIdx.x][1] + cred[threadIdx.x][2] + cred[threadIdx.x][3];
+      if (tot != 0) atomicAdd(counts + threadIdx.x, (unsigned long long)tot);
+    }
+  }
   // a plain read first: most blocks do not raise the running maximum
   if (threadIdx.x == 0 && amax_slot != nullptr &&
       r > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
@@ -353,8 +395,8 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
     int64_t blocks = (n + per_block - 1) / per_block;
     if (blocks < 1) blocks = 1;
     if (blocks > kTensorMaxBlocks) blocks = kTensorMaxBlocks;
-    hipLaunchKernelGGL((quant_tensor_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(kTensorThreads), 0, st, x, n,
-                       scale, reinterpret_cast<uint32_t*>(amax_slot), q);
+    hipLaunchKernelGGL((quant_tensor_kernel<FMT, BF16, false>), dim3((unsigned)blocks), dim3(kTensorThreads), 0, st,
+                       x, n, scale, reinterpret_cast<uint32_t*>(amax_slot), q, nullptr);
   } else if (gran == FP8_SCALE_TILE_1x128) {
     const int64_t blocks = ((rows + kTileRows - 1) / kTileRows) * (((cols >> 7) + 3) / 4);
     hipLaunchKernelGGL((quant_tile_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, q,
@@ -408,4 +450,36 @@ extern "C" int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
               : launch_quant<FP8_E4M3, false>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st);
   return bf ? launch_quant<FP8_E5M2, true>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st)
             : launch_quant<FP8_E5M2, false>(x, rows, cols, granularity, scale, amax_slot, q, scale_inv_out, st);
+}
+
+extern "C" int fp8_quantize_diag(const void* x, int x_dtype, int64_t rows, int64_t cols, int fmt, const float* scale,
+                                 float* amax_slot, uint8_t* q, unsigned long long* counts, void* stream) {
+  SFP8_REQUIRE(rows >= 0 && cols >= 0, FP8_ERR_SHAPE, "fp8_quantize_diag: negative shape (%lld, %lld)",
+               (long long)rows, (long long)cols);
+  SFP8_REQUIRE(x_dtype == HP_F32 || x_dtype == HP_BF16, FP8_ERR_DTYPE, "fp8_quantize_diag: x_dtype %d", x_dtype);
+  SFP8_REQUIRE(fmt == FP8_E4M3 || fmt == FP8_E5M2, FP8_ERR_ARG, "fp8_quantize_diag: fmt %d", fmt);
+  SFP8_REQUIRE(scale != nullptr && counts != nullptr, FP8_ERR_ARG, "fp8_quantize_diag: null scale or counts");
+  SFP8_REQUIRE(aligned4(scale) && (amax_slot == nullptr || aligned4(amax_slot)) &&
+                   (reinterpret_cast<uintptr_t>(counts) & 7) == 0,
+               FP8_ERR_ARG, "fp8_quantize_diag: scale / amax_slot must be 4-byte and counts 8-byte aligned");
+  const int64_t n = rows * cols;
+  if (n == 0) return FP8_OK;
+  SFP8_REQUIRE(x != nullptr && q != nullptr, FP8_ERR_ARG, "fp8_quantize_diag: null x or q");
+  SFP8_REQUIRE(aligned16(x) && aligned16(q), FP8_ERR_ARG, "fp8_quantize_diag: x and q must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t per_block = (int64_t)kTensorThreads * kTensorPieces * 8;
+  int64_t blocks = (n + per_block - 1) / per_block;
+  if (blocks < 1) blocks = 1;
+  if (blocks > kTensorMaxBlocks) blocks = kTensorMaxBlocks;
+  const dim3 grid((unsigned)blocks), block(kTensorThreads);
+  uint32_t* slot = reinterpret_cast<uint32_t*>(amax_slot);
+  const bool bf = x_dtype == HP_BF16;
+  if (fmt == FP8_E4M3) {
+    if (bf) hipLaunchKernelGGL((quant_tensor_kernel<FP8_E4M3, true, true>), grid, block, 0, st, x, n, scale, slot, q, counts);
+    else hipLaunchKernelGGL((quant_tensor_kernel<FP8_E4M3, false, true>), grid, block, 0, st, x, n, scale, slot, q, counts);
+  } else {
+    if (bf) hipLaunchKernelGGL((quant_tensor_kernel<FP8_E5M2, true, true>), grid, block, 0, st, x, n, scale, slot, q, counts);
+    else hipLaunchKernelGGL((quant_tensor_kernel<FP8_E5M2, false, true>), grid, block, 0, st, x, n, scale, slot, q, counts);
+  }
+  return check_launch("fp8_quantize_diag");
 }

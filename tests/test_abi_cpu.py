@@ -19,8 +19,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    assert names == sorted(["fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_cast_transpose",
-                            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error"])
+    assert names == sorted(["fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag",
+                            "fp8_cast_transpose", "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -83,6 +83,12 @@ def test_argument_errors_return_before_launch():
     assert lib.fp8_cast_transpose(fake, 1, 4, 4, 0, None, None, fake, fake, None) == sq.FP8_ERR_ARG
     assert lib.fp8_cast_transpose(fake, 2, 4, 4, 0, fake, None, fake, fake, None) == sq.FP8_ERR_DTYPE
     assert lib.fp8_cast_transpose(None, 1, 0, 5, 0, fake, None, None, None, None) == sq.FP8_OK
+    # quantize with diagnostics: counts required and 8-byte aligned
+    qd = lib.fp8_quantize_diag
+    assert qd(fake, 1, 4, 128, 0, fake, None, fake, None, None) == sq.FP8_ERR_ARG
+    assert qd(fake, 1, 4, 128, 0, fake, None, fake, ctypes.c_void_p(0x100004), None) == sq.FP8_ERR_ARG
+    assert qd(fake, 3, 4, 128, 0, fake, None, fake, fake, None) == sq.FP8_ERR_DTYPE
+    assert qd(None, 1, 0, 128, 0, fake, None, None, fake, None) == sq.FP8_OK
     # blockwise cast-transpose: granularity, shapes that are not multiples of 128, dtype, empty
     ct = lib.fp8_cast_transpose_blockwise
     assert ct(fake, 1, 128, 128, 0, 0, fake, fake, fake, fake, None) == sq.FP8_ERR_ARG

@@ -157,3 +157,33 @@ def test_empty_inputs(sq):
     q, si = sq.fp8_quantize(torch.empty((0, 128), device=DEV), sq.FP8_E4M3, sq.FP8_SCALE_TILE_1x128)
     torch.cuda.synchronize()
     assert q.numel() == 0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("n", [1, 1000, 65536 * 3 + 5])
+def test_quantize_diag_counts(sq, fmt, bf16, n):
+    """Saturated / underflowed / NaN counts match the oracle exactly and accumulate across
+    calls; codes and amax match fp8_quantize."""
+    announce("quantize_diag", ofp8.fmt_name(fmt), "bf16" if bf16 else "f32", n)
+    rng = np.random.default_rng(n + 3 * fmt)
+    x = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 12, n))).astype(np.float32)
+    k = min(n, 6)
+    x[:k] = [np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-30][:k]
+    xt = torch.from_numpy(x)
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+    xs = f32_np(xt)
+    scale = float(np.float32(ofp8.FMAX[fmt]) / np.float32(300.0))  # clips the large tail
+    s = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    slot = torch.zeros(1, dtype=torch.float32, device=DEV)
+    counts = torch.zeros(3, dtype=torch.int64, device=DEV)
+    q = sq.fp8_quantize_diag(xt.to(DEV), fmt, s, counts, amax_slot=slot)
+    q2 = sq.fp8_quantize_diag(xt.to(DEV), fmt, s, counts)
+    torch.cuda.synchronize()
+    want = oq.cast_diagnostics(xs, np.float32(scale), fmt)
+    assert np_of(counts).tolist() == [2 * w for w in want]
+    oq_, oa = oq.quantize_tensor(xs, np.float32(scale), fmt)
+    assert_codes_equal(np_of(q).reshape(-1), oq_, "diag codes")
+    assert_codes_equal(np_of(q2).reshape(-1), oq_, "diag codes (second call)")
+    assert np.isnan(np_of(slot)[0]) == np.isnan(oa)

@@ -270,3 +270,40 @@ def test_block_transpose_is_transpose_of_codes_and_scales():
     q2, s2 = quantize.quantize_block_128x128(x.T, E4M3)  # the same blocks, seen transposed
     assert np.array_equal(qT, q.T) and np.array_equal(sT, s.T)
     assert np.array_equal(qT, q2) and np.array_equal(sT, s2)
+
+
+# --------------------------------------------------------------------------- cast diagnostics
+
+
+def test_diagnostics_worked_example_spike_is_one_saturation():
+    """Worked example: with the scale 448/240, 120 fits and 300 clips at 448 -> one saturation."""
+    rows = [[float(v) for v in r] for r in read_golden("worked_example_scale.txt")]
+    amax, fmax = rows[0][0], rows[0][1]
+    s = f32(fmax) / f32(amax)
+    x = np.array([r[2] for r in rows], np.float32)
+    q, _ = quantize.quantize_tensor(x, s, E4M3)
+    assert quantize.cast_diagnostics(x, s, E4M3) == (1, 0, 0)
+    assert fp8.decode(q, E4M3)[1] == 448.0
+
+
+@pytest.mark.parametrize("fmt,tiny", [(E4M3, -9), (E5M2, -16)])
+def test_diagnostics_underflow_boundary(fmt, tiny):
+    """Half the smallest subnormal ties to the even code 0 (underflow); just above it rounds
+    up to the smallest subnormal; zeros of either sign are not underflows."""
+    half = np.exp2(f32(tiny - 1))
+    x = np.array([half, half * f32(1 + 2 ** -20), -half / 2, 0.0, -0.0, np.exp2(f32(tiny))], np.float32)
+    assert quantize.cast_diagnostics(x, f32(1), fmt) == (0, 2, 0)
+
+
+def test_diagnostics_specials_and_code_consistency():
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal(4096) * 100).astype(np.float32)
+    x[:3] = [np.inf, -np.inf, np.nan]
+    s = f32(2.0)
+    sat, und, nan = quantize.cast_diagnostics(x, s, E4M3)
+    q, _ = quantize.quantize_tensor(x, s, E4M3)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = x * s
+    clipped = np.isfinite(x) & (np.abs(y) > 448)
+    assert nan == 1 and sat == int(clipped.sum()) + 2 and und == 0
+    assert np.all((q[clipped] & 0x7F) == 0x7E)
