@@ -45,8 +45,12 @@ enum { FP8_E4M3 = 0, FP8_E5M2 = 1 };
 /* High-precision input element types. */
 enum { HP_F32 = 0, HP_BF16 = 1 };
 
-/* GEMM output element types ([W] precision paragraph: bf16 rounds to nearest even). */
-enum { OUT_F32 = 0, OUT_BF16 = 1 };
+/* GEMM output element types ([W] precision paragraph: bf16 rounds to nearest even).
+ * OUT_E4M3 / OUT_E5M2 (FP8 codes, the next layer's input) are fp8_gemm_fused only. */
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_E4M3 = 2, OUT_E5M2 = 3 };
+
+/* Activations of the fused GEMM epilogue (fp8_gemm_fused). */
+enum { FP8_ACT_NONE = 0, FP8_ACT_GELU = 1, FP8_ACT_SWIGLU = 2 };
 
 /* Scale granularities ([W] absmax bullet: per tensor, per block; MX: one scale per 32
  * numbers; DeepSeek-V3: per 128 activation values and per 128x128 weight block). */
@@ -214,9 +218,9 @@ int fp8_cast_transpose_blockwise(const void *x, int x_dtype, int64_t rows, int64
  *                        multiplied by sa[kb][m] * sb[n/128][kb] and added to an fp32
  *                        accumulator (promotion every 128 K).
  *     TILE_1x128 x TILE_1x128: a_scale_inv = fp32 [K/128][M], b_scale_inv = fp32 [K/128][N];
-                        each K block's partial sum is multiplied by sa[kb][m] * sb[kb][n]
-                        (the blockwise wgrad, both operands activation-style runs).
-     MX_1x32 x MX_1x32: a_scale_inv = uint8 e8m0 [K/32][M], b_scale_inv = uint8 e8m0
+ *                        each K block's partial sum is multiplied by sa[kb][m] * sb[kb][n]
+ *                        (the blockwise wgrad, both operands activation-style runs).
+ *     MX_1x32 x MX_1x32: a_scale_inv = uint8 e8m0 [K/32][M], b_scale_inv = uint8 e8m0
  *                        [K/32][N] (as fp8_quantize writes them); the matrix cores apply
  *                        2^(ea - 127) * 2^(eb - 127) per 32-long run.
  *   Products are exact; the matrix cores sum runs of 8 products in a fixed-point window
@@ -229,6 +233,41 @@ int fp8_cast_transpose_blockwise(const void *x, int x_dtype, int64_t rows, int64
 int fp8_gemm(const uint8_t *A, int fmt_a, const void *a_scale_inv, int gran_a,
              const uint8_t *B, int fmt_b, const void *b_scale_inv, int gran_b, void *C,
              int c_dtype, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * fp8_gemm_fused -- fp8_gemm with the step after the GEMM fused into its epilogue.
+ *   [T] module tour cell (te.Linear(bias=True): Y = X W^T + b) and plain-PyTorch block cell
+ *   (nn.GELU between the MLP's linears: the exact form x * Phi(x)); [W] MoE exercise (a
+ *   SwiGLU expert: silu(x Wg^T) * (x Wu^T)); [L] Part 01 (the amax of every FP8 tensor is
+ *   recorded each step, here the output's, for the next layer's delayed scale).
+ *
+ *   A, B, scales, granularities, M, N, K: as fp8_gemm (N = the pre-activation width).
+ *   Per output element, in fp32, in this order:
+ *     v = the dequantised GEMM result (exactly fp8_gemm's fp32 value)
+ *     v = v + bias[n]             if bias != NULL (bias_dtype HP_F32 or HP_BF16, [N])
+ *     aux[m][n] = bf16(v)         if aux != NULL (bf16 [M][N], round to nearest even)
+ *     act = FP8_ACT_NONE:   y[m][n] = v
+ *           FP8_ACT_GELU:   y[m][n] = v * Phi(v)   (Phi = standard normal CDF)
+ *           FP8_ACT_SWIGLU: y[m][f] = silu(v[m][2f]) * v[m][2f+1],  silu(g) = g / (1 + e^-g);
+ *                           B's rows interleave gate and up units (row 2f = gate f,
+ *                           row 2f+1 = up f); C has N/2 columns; N must be even.
+ *   C (row-major, N or N/2 columns) by c_dtype:
+ *     OUT_F32, OUT_BF16:    y (bf16: round to nearest even)
+ *     OUT_E4M3, OUT_E5M2:   code = enc(fp32(y * c_scale[0])) with fp8_quantize's saturating
+ *                           cast (NaN -> sign | 0x7F), and c_amax[0] = max(c_amax[0], max |y|)
+ *                           (an atomic max, so c_amax accumulates over calls until the
+ *                           recipe update reads and clears it).
+ *   Alignment: C, aux 16-byte aligned; bias 4-byte (fp32) or 2-byte (bf16) aligned;
+ *   c_scale, c_amax 4-byte aligned.  c_scale / c_amax are ignored for fp32 / bf16 output.
+ *   Errors: as fp8_gemm; FP8_ERR_ARG (bad act, misaligned or missing c_scale / c_amax for
+ *           FP8 output), FP8_ERR_SHAPE (SwiGLU with odd N), FP8_ERR_DTYPE (c_dtype,
+ *           bias_dtype).
+ */
+int fp8_gemm_fused(const uint8_t *A, int fmt_a, const void *a_scale_inv, int gran_a,
+                   const uint8_t *B, int fmt_b, const void *b_scale_inv, int gran_b,
+                   const void *bias, int bias_dtype, int act, void *aux, void *C, int c_dtype,
+                   const float *c_scale, float *c_amax, int64_t M, int64_t N, int64_t K,
+                   void *stream);
 
 /* Text describing the calling thread's last non-OK status ("" if none).  Owned by the
  * library; valid until the next call on the same thread. */

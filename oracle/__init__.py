@@ -21,8 +21,9 @@ Sources (cited by page title and section):
   57,344, E4M3 for weights/activations and E5M2 for gradients) and the
   accumulation-precision bullet (64 + 3 = 64; 100 threes; promotion to fp32).
 * Transformer Engine tutorial (juicytalk.now): the DelayedScaling recipe
-  (HYBRID format, amax_history_len=16, amax_compute_algo="max") and the FP8
-  metadata readback (scale, amax_history[0, :4]).
+  (HYBRID format, amax_history_len=16, amax_compute_algo="max"), the FP8
+  metadata readback (scale, amax_history[0, :4]), the module tour
+  (te.Linear(bias=True)) and the plain-PyTorch block (nn.GELU in the MLP).
 
 Modules
 -------
@@ -30,6 +31,7 @@ fp8        FP8 E4M3/E5M2 decode + saturating RNE encode, bf16 RNE, e8m0.
 recipe     amax, delayed-scaling state and update, current-scaling scale rules.
 quantize   per-tensor, 1x128, 128x128 and MX 1x32 quantizers; cast-transpose.
 gemm       fp64 GEMM over dequantized operands plus the error-bound matrix.
+epilogue   bias, exact GELU, SwiGLU over interleaved gate/up columns, FP8 output + amax.
 absmax     int8 absmax example of the course page (a building-block check).
 accum      FP8-rounded running sums (the accumulation-precision example).
 
@@ -38,4 +40,4 @@ closed forms, invariants, library routines and brute force.  Readings taken
 where the pages are silent are listed in each module's docstring.
 """
 
-from . import fp8, recipe, quantize, gemm, absmax, accum  # noqa: F401
+from . import fp8, recipe, quantize, gemm, epilogue, absmax, accum  # noqa: F401

@@ -26,13 +26,14 @@ from .build import LIBDIR, LIBNAME
 
 FP8_E4M3, FP8_E5M2 = 0, 1
 HP_F32, HP_BF16 = 0, 1
-OUT_F32, OUT_BF16 = 0, 1
+OUT_F32, OUT_BF16, OUT_E4M3, OUT_E5M2 = 0, 1, 2, 3
+FP8_ACT_NONE, FP8_ACT_GELU, FP8_ACT_SWIGLU = 0, 1, 2
 FP8_SCALE_TENSOR, FP8_SCALE_TILE_1x128, FP8_SCALE_BLOCK_128x128, FP8_SCALE_MX_1x32 = 0, 1, 2, 3
 FP8_AMAX_ALGO_MAX = 0
 FP8_OK, FP8_ERR_ARG, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_DEVICE, FP8_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag", "fp8_cast_transpose",
-            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error")
+            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_gemm_fused", "fp8_last_error")
 
 LIB_PATH = os.path.join(LIBDIR, LIBNAME)
 
@@ -56,6 +57,8 @@ def _load() -> ctypes.CDLL:
     lib.fp8_cast_transpose.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.fp8_cast_transpose_blockwise.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_gemm.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, i64, i64, i64, vp]
+    lib.fp8_gemm_fused.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, i32, vp, vp, i32, vp, vp, i64, i64,
+                                   i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
     for name in ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag", "fp8_cast_transpose",
                  "fp8_cast_transpose_blockwise", "fp8_gemm"):
@@ -225,6 +228,35 @@ def fp8_gemm(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_a: int
         C = torch.empty((M, N), dtype=dt, device=A.device)
     _check(lib.fp8_gemm(_ptr(A), fmt_a, _ptr(a_scale_inv), gran_a, _ptr(B), fmt_b, _ptr(b_scale_inv), gran_b,
                         _ptr(C), out_dtype, M, N, K, _stream(A)))
+    return C
+
+
+_OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_E4M3: torch.uint8, OUT_E5M2: torch.uint8}
+
+
+def fp8_gemm_fused(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_a: int, B: torch.Tensor, fmt_b: int,
+                   b_scale_inv: torch.Tensor, gran_b: int, out_dtype: int = OUT_BF16,
+                   bias: Optional[torch.Tensor] = None, act: int = FP8_ACT_NONE, aux: Optional[torch.Tensor] = None,
+                   c_scale: Optional[torch.Tensor] = None, c_amax: Optional[torch.Tensor] = None,
+                   C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp8_gemm with bias, optional bf16 pre-activation copy (aux), GELU / SwiGLU and an
+    fp32 / bf16 / FP8 output (FP8: codes under c_scale, amax max-reduced into c_amax)."""
+    _contig(A, "A")
+    _contig(B, "B")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: {K} vs {K2}")
+    if C is None:
+        cols = N // 2 if act == FP8_ACT_SWIGLU else N
+        C = torch.empty((M, cols), dtype=_OUT_TORCH.get(out_dtype, torch.float32), device=A.device)
+    bias_dt = HP_F32
+    if bias is not None:
+        _contig(bias, "bias")
+        bias_dt = _hp_dtype(bias)
+    _check(lib.fp8_gemm_fused(_ptr(A), fmt_a, _ptr(a_scale_inv), gran_a, _ptr(B), fmt_b, _ptr(b_scale_inv), gran_b,
+                              _ptr(bias), bias_dt, act, _ptr(aux), _ptr(C), out_dtype, _ptr(c_scale), _ptr(c_amax),
+                              M, N, K, _stream(A)))
     return C
 
 

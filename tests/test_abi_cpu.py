@@ -20,7 +20,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag",
-                            "fp8_cast_transpose", "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_last_error"])
+                            "fp8_cast_transpose", "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_gemm_fused",
+                            "fp8_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,7 +37,8 @@ def test_header_constants_match_binding():
     import scaled_quantize_gemm_amd as sq
 
     src = open(HEADER).read()
-    for name in ["FP8_E4M3", "FP8_E5M2", "HP_F32", "HP_BF16", "OUT_F32", "OUT_BF16", "FP8_SCALE_TENSOR",
+    for name in ["FP8_E4M3", "FP8_E5M2", "HP_F32", "HP_BF16", "OUT_F32", "OUT_BF16", "OUT_E4M3", "OUT_E5M2",
+                 "FP8_ACT_NONE", "FP8_ACT_GELU", "FP8_ACT_SWIGLU", "FP8_SCALE_TENSOR",
                  "FP8_SCALE_TILE_1x128", "FP8_SCALE_BLOCK_128x128", "FP8_SCALE_MX_1x32", "FP8_OK", "FP8_ERR_ARG",
                  "FP8_ERR_SHAPE", "FP8_ERR_DTYPE", "FP8_ERR_DEVICE", "FP8_ERR_LAUNCH"]:
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
@@ -107,6 +109,18 @@ def test_argument_errors_return_before_launch():
     assert lib.fp8_gemm(fake, 0, fake, 0, fake, 0, fake, 0, fake, 7, 4, 4, 128, None) == sq.FP8_ERR_DTYPE
     assert lib.fp8_gemm(fake, 0, fake, 0, fake, 0, fake, 0, fake, 0, 0, 4, 128, None) == sq.FP8_OK
     assert lib.fp8_gemm(fake, 2, fake, 0, fake, 0, fake, 0, fake, 0, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    # fused gemm: bad act, SwiGLU with odd N, FP8 output without scale / amax, bad out and bias
+    # dtypes, C not 16-byte aligned, bad granularity pair, empty
+    fg = lib.fp8_gemm_fused
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 9, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 2, None, fake, 0, None, None, 4, 5, 128, None) == sq.FP8_ERR_SHAPE
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 0, None, fake, 2, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 0, None, fake, 4, None, None, 4, 4, 128, None) == sq.FP8_ERR_DTYPE
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, fake, 5, 0, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_DTYPE
+    c4 = ctypes.c_void_p(0x100004)
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 0, None, c4, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 2, None, 0, 0, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 1, None, fake, 2, None, None, 0, 4, 128, None) == sq.FP8_OK
     # recipe update
     fmts = (ctypes.c_int * 2)(0, 1)
     assert lib.fp8_recipe_update(fake, fake, fake, fmts, 0, 16, 0, 0, None) == sq.FP8_ERR_ARG
