@@ -204,6 +204,39 @@ int fp8_cast_transpose_blockwise(const void *x, int x_dtype, int64_t rows, int64
                                  float *qT_scale_inv, void *stream);
 
 /*
+ * fp8_layernorm_quantize -- LayerNorm whose output goes straight to FP8 (no high-precision
+ *   copy of it is written).
+ *   [T] module tour cell (te.LayerNorm; te.LayerNormLinear and te.LayerNormMLP feed the norm
+ *   into the FP8 linear) and plain-PyTorch block cell (nn.LayerNorm before attention and the
+ *   MLP); [L] Part 01 and [W] absmax bullet for the scales, as fp8_quantize.
+ *
+ *   x          device, x_dtype HP_F32 or HP_BF16, [rows][cols]
+ *   gamma      device, w_dtype HP_F32 or HP_BF16, [cols]; beta the same or NULL (no shift)
+ *   eps        >= 0 (nn.LayerNorm's default is 1e-5)
+ *   Per row, in fp32: mean = sum(x) / cols; var = sum((x - mean)^2) / cols (biased);
+ *   rs = 1 / sqrt(var + eps); y = (x - mean) * rs * gamma + beta.
+ *   y is then cast exactly as fp8_quantize casts an input at `granularity`:
+ *     FP8_SCALE_TENSOR:   codes = enc(fp32(y * scale[0])); amax_slot (may be NULL) max-reduced
+ *                         with max |y|; scale_inv_out unused.
+ *     FP8_SCALE_TILE_1x128: per 1x128 run of y, s = fmax / amax; scale_inv_out = fp32
+ *                         [cols/128][rows].
+ *     FP8_SCALE_MX_1x32:  per 1x32 run, e8m0 code and 2^-E; scale_inv_out = uint8
+ *                         [cols/32][rows].
+ *   q          device uint8 [rows][cols]
+ *   mu, rsigma device fp32 [rows] (the row's mean and rs, for the backward), or NULL.
+ *   cols % 8 == 0 (TENSOR), % 128 (TILE_1x128), % 32 (MX_1x32); cols <= 8192.
+ *   Alignment: x, q, gamma, beta 16-byte aligned; scale, amax_slot, fp32 scales, mu, rsigma
+ *   4-byte aligned.  Empty inputs are a no-op.
+ *   Errors: FP8_ERR_ARG (null pointer, bad enum or granularity BLOCK_128x128, misalignment,
+ *           eps < 0), FP8_ERR_SHAPE (cols not a multiple of the run, cols > 8192),
+ *           FP8_ERR_DTYPE (x_dtype, w_dtype).
+ */
+int fp8_layernorm_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols,
+                           const void *gamma, const void *beta, int w_dtype, float eps, int fmt,
+                           int granularity, const float *scale, float *amax_slot, uint8_t *q,
+                           void *scale_inv_out, float *mu, float *rsigma, void *stream);
+
+/*
  * fp8_gemm -- C[M][N] = sum_k deq(A[m][k]) * deq(B[n][k])  (C = A . B^T, Y = X W^T).
  *   [W] FP8 bullet (matmuls run in FP8) and accumulation-precision bullet (FP8 products are
  *   summed in a wider accumulator and partial sums are promoted to fp32 at fixed
@@ -241,7 +274,9 @@ int fp8_gemm(const uint8_t *A, int fmt_a, const void *a_scale_inv, int gran_a,
  *   SwiGLU expert: silu(x Wg^T) * (x Wu^T)); [L] Part 01 (the amax of every FP8 tensor is
  *   recorded each step, here the output's, for the next layer's delayed scale).
  *
- *   A, B, scales, granularities, M, N, K: as fp8_gemm (N = the pre-activation width).
+ *   A, B, scales, granularities, M, N, K: as fp8_gemm (N = the pre-activation width), except
+ *   that B must be E4M3 (B is a weight, or an activation for wgrad: E4M3 in every recipe of
+ *   [W] FP8 bullet); A may be E4M3 or E5M2.
  *   Per output element, in fp32, in this order:
  *     v = the dequantised GEMM result (exactly fp8_gemm's fp32 value)
  *     v = v + bias[n]             if bias != NULL (bias_dtype HP_F32 or HP_BF16, [N])
@@ -259,8 +294,8 @@ int fp8_gemm(const uint8_t *A, int fmt_a, const void *a_scale_inv, int gran_a,
  *                           recipe update reads and clears it).
  *   Alignment: C, aux 16-byte aligned; bias 4-byte (fp32) or 2-byte (bf16) aligned;
  *   c_scale, c_amax 4-byte aligned.  c_scale / c_amax are ignored for fp32 / bf16 output.
- *   Errors: as fp8_gemm; FP8_ERR_ARG (bad act, misaligned or missing c_scale / c_amax for
- *           FP8 output), FP8_ERR_SHAPE (SwiGLU with odd N), FP8_ERR_DTYPE (c_dtype,
+ *   Errors: as fp8_gemm; FP8_ERR_ARG (fmt_b not E4M3, bad act, misaligned or missing c_scale /
+ *           c_amax for FP8 output), FP8_ERR_SHAPE (SwiGLU with odd N), FP8_ERR_DTYPE (c_dtype,
  *           bias_dtype).
  */
 int fp8_gemm_fused(const uint8_t *A, int fmt_a, const void *a_scale_inv, int gran_a,

@@ -32,6 +32,7 @@ recipe     amax, delayed-scaling state and update, current-scaling scale rules.
 quantize   per-tensor, 1x128, 128x128 and MX 1x32 quantizers; cast-transpose.
 gemm       fp64 GEMM over dequantized operands plus the error-bound matrix.
 epilogue   bias, exact GELU, SwiGLU over interleaved gate/up columns, FP8 output + amax.
+layernorm  LayerNorm (biased variance, eps) followed by the quantizers.
 absmax     int8 absmax example of the course page (a building-block check).
 accum      FP8-rounded running sums (the accumulation-precision example).
 
@@ -40,4 +41,4 @@ closed forms, invariants, library routines and brute force.  Readings taken
 where the pages are silent are listed in each module's docstring.
 """
 
-from . import fp8, recipe, quantize, gemm, epilogue, absmax, accum  # noqa: F401
+from . import fp8, recipe, quantize, gemm, epilogue, layernorm, absmax, accum  # noqa: F401

@@ -33,7 +33,8 @@ FP8_AMAX_ALGO_MAX = 0
 FP8_OK, FP8_ERR_ARG, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_DEVICE, FP8_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag", "fp8_cast_transpose",
-            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_gemm_fused", "fp8_last_error")
+            "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_gemm_fused", "fp8_layernorm_quantize",
+            "fp8_last_error")
 
 LIB_PATH = os.path.join(LIBDIR, LIBNAME)
 
@@ -57,6 +58,8 @@ def _load() -> ctypes.CDLL:
     lib.fp8_cast_transpose.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.fp8_cast_transpose_blockwise.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.fp8_gemm.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, i64, i64, i64, vp]
+    lib.fp8_layernorm_quantize.argtypes = [vp, i32, i64, i64, vp, vp, i32, ctypes.c_float, i32, i32, vp, vp, vp, vp,
+                                           vp, vp, vp]
     lib.fp8_gemm_fused.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, i32, vp, vp, i32, vp, vp, i64, i64,
                                    i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
@@ -229,6 +232,31 @@ def fp8_gemm(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_a: int
     _check(lib.fp8_gemm(_ptr(A), fmt_a, _ptr(a_scale_inv), gran_a, _ptr(B), fmt_b, _ptr(b_scale_inv), gran_b,
                         _ptr(C), out_dtype, M, N, K, _stream(A)))
     return C
+
+
+def fp8_layernorm_quantize(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor], eps: float, fmt: int,
+                           granularity: int = FP8_SCALE_TENSOR, scale: Optional[torch.Tensor] = None,
+                           amax_slot: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                           scale_inv_out: Optional[torch.Tensor] = None, mu: Optional[torch.Tensor] = None,
+                           rsigma: Optional[torch.Tensor] = None):
+    """LayerNorm over the last dim of x [rows][cols] cast to FP8 -> (q, scale_inv_out or None)."""
+    _contig(x, "x")
+    _contig(gamma, "gamma")
+    rows, cols = _as2d(x)
+    if beta is not None:
+        _contig(beta, "beta")
+        if beta.dtype != gamma.dtype:
+            raise TypeError("gamma and beta must share a dtype")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale_inv_out is None and granularity == FP8_SCALE_TILE_1x128:
+        scale_inv_out = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
+    elif scale_inv_out is None and granularity == FP8_SCALE_MX_1x32:
+        scale_inv_out = torch.empty((cols // 32, rows), dtype=torch.uint8, device=x.device)
+    _check(lib.fp8_layernorm_quantize(_ptr(x), _hp_dtype(x), rows, cols, _ptr(gamma), _ptr(beta), _hp_dtype(gamma),
+                                      float(eps), fmt, granularity, _ptr(scale), _ptr(amax_slot), _ptr(q),
+                                      _ptr(scale_inv_out), _ptr(mu), _ptr(rsigma), _stream(x)))
+    return q, scale_inv_out
 
 
 _OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_E4M3: torch.uint8, OUT_E5M2: torch.uint8}

@@ -18,10 +18,15 @@
 //      max-reduced into an amax slot for the delayed recipe ("Transformer Scaling" lesson,
 //      Part 01: each tensor's amax is recorded every step).
 //
-// The kernels call, per lane, for runs of W adjacent columns gn .. gn+W-1 (gn % W == 0) of
-// one row gm:  pre() (bias), aux(), out();  and finish() once at the end (amax reduction).
-// `full` means all W columns exist and a W-wide vector store is aligned (N % W == 0).
+// The kernels run their store loop inside with_act(), which calls it with the activation as a
+// compile-time constant (a runtime test inside the unrolled loop let the compiler evaluate
+// the GELU of every element whatever the activation, and select), and call, per lane, for
+// runs of W adjacent columns gn .. gn+W-1 (gn % W == 0) of one row gm:  pre() (bias), aux(),
+// out<ACT>();  and finish() once at the end (amax reduction).  `full` means all W columns
+// exist and a W-wide vector store is aligned (N % W == 0).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -60,7 +65,21 @@ struct Epilogue {
     if constexpr (kFp8) cs = *p.c_scale;
   }
 
-  __device__ __forceinline__ bool pairs() const { return FUSED && p.act == FP8_ACT_SWIGLU; }
+  // f(integral_constant<int, ACT>) with the launch's activation
+  template <class F>
+  __device__ __forceinline__ void with_act(F&& f) const {
+    if constexpr (FUSED) {
+      if (p.act == FP8_ACT_GELU) {
+        f(std::integral_constant<int, FP8_ACT_GELU>{});
+        return;
+      }
+      if (p.act == FP8_ACT_SWIGLU) {
+        f(std::integral_constant<int, FP8_ACT_SWIGLU>{});
+        return;
+      }
+    }
+    f(std::integral_constant<int, FP8_ACT_NONE>{});
+  }
 
   // bias[gn + i] for i < W (0 where absent)
   template <int W>
@@ -96,26 +115,22 @@ struct Epilogue {
   }
 
   // activation and the output store
-  template <int W>
+  template <int ACT, int W>
   __device__ __forceinline__ void out(float (&v)[W], int gm, int gn, int N, bool full) {
-    if constexpr (FUSED) {
-      if (p.act == FP8_ACT_SWIGLU) {
-        static_assert(W % 2 == 0 || W == 1, "SwiGLU needs column pairs");
-        if constexpr (W >= 2) {
-          float o[W / 2];
+    if constexpr (ACT == FP8_ACT_SWIGLU) {
+      static_assert(W % 2 == 0, "SwiGLU needs column pairs");
+      float o[W / 2];
 #pragma unroll
-          for (int i = 0; i < W / 2; ++i) o[i] = swiglu(v[2 * i], v[2 * i + 1]);
-          // output column gn/2 + i exists iff its up column gn + 2i + 1 does
-          emit<W / 2>(o, (size_t)gm * (N / 2) + gn / 2, full, (N - gn) / 2);
-        }
-        return;
-      }
-      if (p.act == FP8_ACT_GELU) {
+      for (int i = 0; i < W / 2; ++i) o[i] = swiglu(v[2 * i], v[2 * i + 1]);
+      // output column gn/2 + i exists iff its up column gn + 2i + 1 does
+      emit<W / 2>(o, (size_t)gm * (N / 2) + gn / 2, full, (N - gn) / 2);
+    } else {
+      if constexpr (ACT == FP8_ACT_GELU) {
 #pragma unroll
         for (int i = 0; i < W; ++i) v[i] = gelu_exact(v[i]);
       }
+      emit<W>(v, (size_t)gm * N + gn, full, N - gn);
     }
-    emit<W>(v, (size_t)gm * N + gn, full, N - gn);
   }
 
   // all lanes of the wave: fold the lanes' amax into the slot

@@ -3,14 +3,19 @@
 #include "gemm_kernels.h"
 
 namespace sfp8 {
-// one per output type, each in its own translation unit (gemm_fused_<type>.hip)
+// one per (output type, mode pair), each in its own translation unit (gemm_fused_<type>_<pair>.hip):
+// tm = per-tensor and MX, bt = the two blockwise modes
 #define SFP8_FUSED_DECL(name)                                                                                   \
   int name(int mode, int fa, int fb, const uint8_t* A, const uint8_t* B, const void* sa, const void* sb,        \
            const EpiParams& ep, int M, int N, int K, hipStream_t st);
-SFP8_FUSED_DECL(gemm_fused_f32)
-SFP8_FUSED_DECL(gemm_fused_bf16)
-SFP8_FUSED_DECL(gemm_fused_e4m3)
-SFP8_FUSED_DECL(gemm_fused_e5m2)
+SFP8_FUSED_DECL(gemm_fused_f32_tm)
+SFP8_FUSED_DECL(gemm_fused_f32_bt)
+SFP8_FUSED_DECL(gemm_fused_bf16_tm)
+SFP8_FUSED_DECL(gemm_fused_bf16_bt)
+SFP8_FUSED_DECL(gemm_fused_e4m3_tm)
+SFP8_FUSED_DECL(gemm_fused_e4m3_bt)
+SFP8_FUSED_DECL(gemm_fused_e5m2_tm)
+SFP8_FUSED_DECL(gemm_fused_e5m2_bt)
 #undef SFP8_FUSED_DECL
 }  // namespace sfp8
 
@@ -24,6 +29,8 @@ extern "C" int fp8_gemm_fused(const uint8_t* A, int fmt_a, const void* a_scale_i
   int mode = -1;
   const int rc = gemm_check(what, A, fmt_a, a_scale_inv, gran_a, B, fmt_b, b_scale_inv, gran_b, M, N, K, mode);
   if (rc != FP8_OK) return rc;
+  SFP8_REQUIRE(fmt_b == FP8_E4M3, FP8_ERR_ARG, "%s: B must be E4M3 (weights and activations are E4M3 in every recipe)",
+               what);
   SFP8_REQUIRE(c_dtype == OUT_F32 || c_dtype == OUT_BF16 || c_dtype == OUT_E4M3 || c_dtype == OUT_E5M2,
                FP8_ERR_DTYPE, "%s: c_dtype %d", what, c_dtype);
   SFP8_REQUIRE(act == FP8_ACT_NONE || act == FP8_ACT_GELU || act == FP8_ACT_SWIGLU, FP8_ERR_ARG, "%s: act %d", what,
@@ -50,10 +57,19 @@ extern "C" int fp8_gemm_fused(const uint8_t* A, int fmt_a, const void* a_scale_i
   ep.act = act;
   hipStream_t st = (hipStream_t)stream;
   const int m = (int)M, n = (int)N, k = (int)K;
+  const bool tm = mode == MODE_TENSOR || mode == MODE_MX;
   switch (c_dtype) {
-    case OUT_F32: return gemm_fused_f32(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m, n, k, st);
-    case OUT_BF16: return gemm_fused_bf16(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m, n, k, st);
-    case OUT_E4M3: return gemm_fused_e4m3(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m, n, k, st);
-    default: return gemm_fused_e5m2(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m, n, k, st);
+    case OUT_F32:
+      return (tm ? gemm_fused_f32_tm : gemm_fused_f32_bt)(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m,
+                                                        n, k, st);
+    case OUT_BF16:
+      return (tm ? gemm_fused_bf16_tm : gemm_fused_bf16_bt)(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m,
+                                                          n, k, st);
+    case OUT_E4M3:
+      return (tm ? gemm_fused_e4m3_tm : gemm_fused_e4m3_bt)(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m,
+                                                          n, k, st);
+    default:
+      return (tm ? gemm_fused_e5m2_tm : gemm_fused_e5m2_bt)(mode, fmt_a, fmt_b, A, B, a_scale_inv, b_scale_inv, ep, m,
+                                                          n, k, st);
   }
 }

@@ -202,29 +202,32 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
   Epilogue<OUT, FUSED> epi(ep);
   float s = 1.0f;
   if constexpr (MODE == MODE_TENSOR) s = *static_cast<const float*>(sa_p) * *static_cast<const float*>(sb_p);
+  epi.with_act([&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-  for (int j = 0; j < Cfg::TN; ++j) {
-    const int gn = n0 + wn * Cfg::WN + 16 * j + r;
-    float b[1];
-    epi.template bias<1>(gn, N, b);
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int gn = n0 + wn * Cfg::WN + 16 * j + r;
+      float b[1];
+      epi.template bias<1>(gn, N, b);
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
+      for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int gm = m0 + wm * Cfg::WM + 16 * i + 4 * g + jj;
-        const bool in = gm < M && gn < N;
-        float v[1] = {MODE == MODE_TENSOR ? acc[i][j][jj] * s : acc[i][j][jj]};
-        epi.pre(v, b);
-        if (in) epi.aux(v, gm, gn, N, true);
-        if (epi.pairs()) {
-          // SwiGLU: the up value of an even (gate) column is held by the next lane
-          float w[2] = {v[0], __shfl_xor(v[0], 1, 64)};
-          if (in && (r & 1) == 0) epi.out(w, gm, gn, N, true);
-        } else if (in) {
-          epi.out(v, gm, gn, N, true);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int gm = m0 + wm * Cfg::WM + 16 * i + 4 * g + jj;
+          const bool in = gm < M && gn < N;
+          float v[1] = {MODE == MODE_TENSOR ? acc[i][j][jj] * s : acc[i][j][jj]};
+          epi.pre(v, b);
+          if (in) epi.aux(v, gm, gn, N, true);
+          if constexpr (ACT == FP8_ACT_SWIGLU) {
+            // the up value of an even (gate) column is held by the next lane
+            float w[2] = {v[0], __shfl_xor(v[0], 1, 64)};
+            if (in && (r & 1) == 0) epi.template out<ACT>(w, gm, gn, N, true);
+          } else if (in) {
+            epi.template out<ACT>(v, gm, gn, N, true);
+          }
         }
-      }
-  }
+    }
+  });
   epi.finish(lane);
 }
 
@@ -588,21 +591,24 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
   const bool pair = (N & 1) == 0 && gn + 1 < N;  // both columns present, pair store aligned
   float b[2];
   epi.template bias<2>(gn, N, b);
+  epi.with_act([&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
+    for (int e = 0; e < 16; ++e)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gm = m0 + grp * 128 + 4 * (8 * (e >> 2) + 4 * g + (e & 3)) + i;
-      if (gm >= M) continue;
-      float v[2] = {acc[i][0][e], acc[i][1][e]};
-      if constexpr (MODE == MODE_TENSOR) {
-        v[0] *= scale;
-        v[1] *= scale;
+      for (int i = 0; i < 4; ++i) {
+        const int gm = m0 + grp * 128 + 4 * (8 * (e >> 2) + 4 * g + (e & 3)) + i;
+        if (gm >= M) continue;
+        float v[2] = {acc[i][0][e], acc[i][1][e]};
+        if constexpr (MODE == MODE_TENSOR) {
+          v[0] *= scale;
+          v[1] *= scale;
+        }
+        epi.pre(v, b);
+        epi.aux(v, gm, gn, N, pair);
+        epi.template out<ACT>(v, gm, gn, N, pair);
       }
-      epi.pre(v, b);
-      epi.aux(v, gm, gn, N, pair);
-      epi.out(v, gm, gn, N, pair);
-    }
+  });
   epi.finish(lane);
 }
 
@@ -855,17 +861,20 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   const bool quad = (N & 3) == 0 && gn + 3 < N;  // all four columns present, store aligned
   float b[4];
   epi.template bias<4>(gn, N, b);
+  epi.with_act([&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gm = m0 + slab_a + 16 * g + 4 * jj + i;
-      if (gm >= M) continue;
-      float v[4] = {acc[i][0][jj], acc[i][1][jj], acc[i][2][jj], acc[i][3][jj]};
-      epi.pre(v, b);
-      epi.aux(v, gm, gn, N, quad);
-      epi.out(v, gm, gn, N, quad);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int gm = m0 + slab_a + 16 * g + 4 * jj + i;
+        if (gm >= M) continue;
+        float v[4] = {acc[i][0][jj], acc[i][1][jj], acc[i][2][jj], acc[i][3][jj]};
+        epi.pre(v, b);
+        epi.aux(v, gm, gn, N, quad);
+        epi.template out<ACT>(v, gm, gn, N, quad);
+      }
+  });
   epi.finish(lane);
 }
 
@@ -952,8 +961,11 @@ static int dispatch_fmt(int fa, int fb, const uint8_t* A, const uint8_t* B, cons
                         const EpiParams& ep, int M, int N, int K, hipStream_t st, const char* what) {
   if (fa == FP8_E4M3 && fb == FP8_E4M3) return launch_gemm<MODE, 0, 0, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
   if (fa == FP8_E5M2 && fb == FP8_E4M3) return launch_gemm<MODE, 1, 0, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
-  if (fa == FP8_E4M3 && fb == FP8_E5M2) return launch_gemm<MODE, 0, 1, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
-  return launch_gemm<MODE, 1, 1, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
+  if constexpr (!FUSED) {  // the fused entry point takes B in E4M3 only (checked on the host)
+    if (fa == FP8_E4M3 && fb == FP8_E5M2) return launch_gemm<MODE, 0, 1, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
+    return launch_gemm<MODE, 1, 1, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
+  }
+  return set_error(FP8_ERR_ARG, "%s: B must be E4M3", what);
 }
 
 template <int OUT, bool FUSED>

@@ -9,32 +9,9 @@
 // Every kernel reads its input once from HBM and writes the codes once: amax is computed
 // from the same registers the cast reads (delayed scaling records it for the next step;
 // the blockwise and MX kernels hold the whole block in registers, reduce, then cast).
-#include "common.h"
+#include "quant_rules.h"
 
 namespace sfp8 {
-
-// ------------------------------------------------------------------ element loaders
-//
-// 8 consecutive elements: one 16-byte load for bf16, two for fp32 (nontemporal: each input
-// is read once).
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, float (&v)[8]) {
-  if constexpr (BF16) {
-    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
-    uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
-    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
-  }
-}
 
 template <bool BF16>
 __device__ __forceinline__ float load_one(const void* __restrict__ base, int64_t i) {
@@ -73,18 +50,6 @@ __device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* red)
 constexpr int kTensorThreads = 256;
 constexpr int kTensorPieces = 2;
 constexpr int64_t kTensorMaxBlocks = 32768;
-
-// 8 values * s -> 8 codes (NaN inputs patched)
-template <int FMT>
-__device__ __forceinline__ u32x2 cast8(const float (&v)[8], float s, uint32_t amax_bits) {
-  uint32_t w0 = cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-  uint32_t w1 = cvt4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
-  if (amax_bits > 0x7F800000u) {
-    w0 = patch_nan4(w0, &v[0]);
-    w1 = patch_nan4(w1, &v[4]);
-  }
-  return u32x2{w0, w1};
-}
 
 // Cast diagnostics (DIAG): per element, saturated = |fp32(x s)| > fmax (so the code was
 // clipped), underflowed = x finite and non-zero but its code is +-0, nan = x is NaN; block
@@ -299,27 +264,6 @@ __global__ void __launch_bounds__(kBlockThreads) quant_block_kernel(const void* 
 // is <= 1.75 (bits <= 0x600000), else e - bias + 1 (bias 8 for E4M3, 15 for E5M2); clamped
 // to [-127, 127]; zero amax -> -127; non-finite amax -> code 255 and multiplier 1.  The
 // multiplier 2^-E is exact, so the product is rounded only once, by the cast.
-
-template <int FMT>
-__device__ __forceinline__ void mx_rule(uint32_t amax_bits, uint32_t& code, float& mult) {
-  if (amax_bits >= 0x7F800000u) {
-    code = 255u;
-    mult = 1.0f;
-    return;
-  }
-  int E;
-  const int ef = (int)(amax_bits >> 23);
-  if (ef == 0) {
-    E = -127;  // zero or subnormal amax: the smallest E already exceeds it
-  } else {
-    const int e = ef - 127;
-    E = e - Fp8Traits<FMT>::mx_bias + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    E = E < -127 ? -127 : (E > 127 ? 127 : E);
-  }
-  code = (uint32_t)(E + 127);
-  // E <= 120 for every finite amax, so 2^-E is a normal float: exponent field 127 - E
-  mult = __uint_as_float((uint32_t)(127 - E) << 23);
-}
 
 // A block covers 4*kMxRowsPerWave rows x 16 runs (512 columns).  Wave w takes rows
 // w*kMxRowsPerWave.. of the block; on each row its 64 lanes read 512 consecutive elements

@@ -21,7 +21,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["fp8_device_check", "fp8_recipe_update", "fp8_quantize", "fp8_quantize_diag",
                             "fp8_cast_transpose", "fp8_cast_transpose_blockwise", "fp8_gemm", "fp8_gemm_fused",
-                            "fp8_last_error"])
+                            "fp8_layernorm_quantize", "fp8_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -115,12 +115,26 @@ def test_argument_errors_return_before_launch():
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 9, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 2, None, fake, 0, None, None, 4, 5, 128, None) == sq.FP8_ERR_SHAPE
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 0, None, fake, 2, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
+    assert fg(fake, 0, fake, 0, fake, 1, fake, 0, None, 0, 0, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 0, None, fake, 4, None, None, 4, 4, 128, None) == sq.FP8_ERR_DTYPE
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, fake, 5, 0, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_DTYPE
     c4 = ctypes.c_void_p(0x100004)
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 0, None, c4, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
     assert fg(fake, 0, fake, 0, fake, 0, fake, 2, None, 0, 0, None, fake, 0, None, None, 4, 4, 128, None) == sq.FP8_ERR_ARG
     assert fg(fake, 0, fake, 0, fake, 0, fake, 0, None, 0, 1, None, fake, 2, None, None, 0, 4, 128, None) == sq.FP8_OK
+    # layernorm + cast: dtypes, BLOCK granularity, cols not a multiple of the run, cols > 8192,
+    # negative eps, missing scale for TENSOR, empty
+    ln = lib.fp8_layernorm_quantize
+    f1 = ctypes.c_float(1e-5)
+    assert ln(fake, 4, 4, 768, fake, None, 1, f1, 0, 0, fake, None, fake, None, None, None, None) == sq.FP8_ERR_DTYPE
+    assert ln(fake, 1, 4, 768, fake, None, 6, f1, 0, 0, fake, None, fake, None, None, None, None) == sq.FP8_ERR_DTYPE
+    assert ln(fake, 1, 4, 768, fake, None, 1, f1, 0, 2, None, None, fake, fake, None, None, None) == sq.FP8_ERR_ARG
+    assert ln(fake, 1, 4, 800, fake, None, 1, f1, 0, 1, None, None, fake, fake, None, None, None) == sq.FP8_ERR_SHAPE
+    assert ln(fake, 1, 4, 8320, fake, None, 1, f1, 0, 0, fake, None, fake, None, None, None, None) == sq.FP8_ERR_SHAPE
+    assert ln(fake, 1, 4, 768, fake, None, 1, ctypes.c_float(-1.0), 0, 0, fake, None, fake, None, None, None,
+              None) == sq.FP8_ERR_ARG
+    assert ln(fake, 1, 4, 768, fake, None, 1, f1, 0, 0, None, None, fake, None, None, None, None) == sq.FP8_ERR_ARG
+    assert ln(None, 1, 0, 768, None, None, 1, f1, 0, 0, None, None, None, None, None, None, None) == sq.FP8_OK
     # recipe update
     fmts = (ctypes.c_int * 2)(0, 1)
     assert lib.fp8_recipe_update(fake, fake, fake, fmts, 0, 16, 0, 0, None) == sq.FP8_ERR_ARG
