@@ -14,15 +14,14 @@
 // l+128, ... (NCH of them, cols <= 512 NCH), so every load and code store of the wave is a
 // contiguous 512-element segment of the row, a 1x32 run is 4 adjacent lanes and a 1x128 run
 // 16 adjacent lanes (shuffle reductions within the group).  Mean and variance are two
-// passes over the registers (no cancellation from a one-pass sum of squares).  8 rows per
-// block; row groups are dealt to the XCDs in contiguous ranges (block b runs on XCD b % 8),
-// so the narrow [cols/32][rows] e8m0 and [cols/128][rows] scale columns of neighbouring row
-// groups fill their cache lines in one L2.
+// passes over the registers (no cancellation from a one-pass sum of squares).
+#include <algorithm>
+
 #include "quant_rules.h"
 
 namespace sfp8 {
 
-constexpr int kLnRows = 8;  // rows (waves) per block
+constexpr int kLnRows = 8;  // waves per block, one row each per step
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -30,114 +29,189 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 8 consecutive gamma / beta values (ordinary loads: every row reads them, they stay cached)
-__device__ __forceinline__ void load8_param(const void* __restrict__ p, bool bf16, int e0, float (&v)[8]) {
-  if (bf16) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + e0);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+// raw 16-byte pieces of one 8-element chunk: 1 for bf16, 2 for fp32
+template <bool BF16>
+struct Chunk {
+  u32x4 w[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const void* __restrict__ x, int64_t e0, Chunk<BF16>& c) {
+  if constexpr (BF16) {
+    c.w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
+    c.w[0] = __builtin_nontemporal_load(p);
+    c.w[1] = __builtin_nontemporal_load(p + 1);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack_chunk(const Chunk<BF16>& c, float (&v)[8]) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = bf16_lo(w[i]);
       v[2 * i + 1] = bf16_hi(w[i]);
     }
   } else {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + e0);
-    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + e0 + 4);
-    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    const uint32_t w[8] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w, c.w[1].x, c.w[1].y, c.w[1].z, c.w[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
   }
 }
 
+// Persistent blocks: the grid is 8 x (blocks per XCD); XCD x (block b runs on XCD b % 8) owns
+// the contiguous range of 8-row groups [G x / 8, G (x + 1) / 8), which its blocks walk with a
+// stride of their count, so the narrow scale columns ([cols/32][rows] e8m0, [cols/128][rows]
+// fp32) of neighbouring groups fill their cache lines in one L2.  gamma and beta sit in LDS as
+// fp32 for the block's lifetime; each wave loads its next row while it normalises the current
+// one, so the row's HBM latency overlaps the reductions and the cast.
 template <int FMT, bool BF16, int GRAN, int NCH>
 __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, const void* __restrict__ beta, int w_bf16, float eps,
-    int64_t rows, int cols, int row_blocks, const float* __restrict__ scale_p, uint32_t* __restrict__ amax_slot,
+    int64_t rows, int cols, int64_t groups, const float* __restrict__ scale_p, uint32_t* __restrict__ amax_slot,
     uint8_t* __restrict__ q, void* __restrict__ sinv, float* __restrict__ mu_out, float* __restrict__ rs_out) {
+  extern __shared__ __attribute__((aligned(16))) float ln_smem[];
+  float* g_s = ln_smem;         // [cols]
+  float* b_s = ln_smem + cols;  // [cols] (zeros without beta)
+  for (int i = threadIdx.x; i < cols; i += 64 * kLnRows) {
+    g_s[i] = w_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(gamma)[i] << 16)
+                    : static_cast<const float*>(gamma)[i];
+    float bv = 0.0f;
+    if (beta != nullptr)
+      bv = w_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(beta)[i] << 16)
+                  : static_cast<const float*>(beta)[i];
+    b_s[i] = bv;
+  }
+  __syncthreads();
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x, xcd = b & 7, idx = b >> 3, per = row_blocks >> 3, rem = row_blocks & 7;
-  const int rb = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  const int64_t row = (int64_t)rb * kLnRows + wave;
-  const bool live = row < rows;   // waves past the last row idle until the block's amax reduction
-  const int nch = live ? cols >> 3 : 0;
-  const int64_t base = row * cols;
-
-  float v[NCH][8];
-  float sum = 0.0f;
-#pragma unroll
-  for (int p = 0; p < NCH; ++p) {
-    const int c = lane + 64 * p;
-    if (c < nch) {
-      load8<BF16>(x, base + 8 * c, v[p]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sum += v[p][i];
-    }
-  }
-  const float mean = wave_sum(sum) / (float)cols;
-  float ssq = 0.0f;
-#pragma unroll
-  for (int p = 0; p < NCH; ++p)
-    if (lane + 64 * p < nch) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[p][i] -= mean;
-        ssq += v[p][i] * v[p][i];
-      }
-    }
-  const float rs = 1.0f / sqrtf(wave_sum(ssq) / (float)cols + eps);
-  if (lane == 0 && live) {
-    if (mu_out != nullptr) mu_out[row] = mean;
-    if (rs_out != nullptr) rs_out[row] = rs;
-  }
-
+  const int nbx = gridDim.x >> 3, xcd = blockIdx.x & 7;
+  const int64_t g_end = groups * (xcd + 1) / 8;
+  const int nch = cols >> 3;
   float s = 1.0f;
   if constexpr (GRAN == FP8_SCALE_TENSOR) s = *scale_p;
   uint32_t lane_amax = 0u;
+
+  // the next row is prefetched when its raw chunks fit beside the current row's values (rows
+  // of at most 4096 columns)
+  constexpr bool PF = NCH <= 8;
+  int64_t grp = groups * xcd / 8 + (blockIdx.x >> 3);
+  int64_t row = grp * kLnRows + wave;
+  Chunk<BF16> raw[PF ? NCH : 1];
+  if constexpr (PF) {
+    if (grp < g_end && row < rows) {
 #pragma unroll
-  for (int p = 0; p < NCH; ++p) {
-    const int c = lane + 64 * p;
-    // whole 4- and 16-lane groups share the branch: nch is a multiple of 4 (MX) / 16 (1x128)
-    if (c >= nch) continue;
-    float g[8];
-    load8_param(gamma, w_bf16, 8 * c, g);
-    if (beta != nullptr) {
-      float bb[8];
-      load8_param(beta, w_bf16, 8 * c, bb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[p][i] = fmaf(v[p][i] * rs, g[i], bb[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] * rs * g[i];
+      for (int p = 0; p < NCH; ++p)
+        if (lane + 64 * p < nch) load_chunk<BF16>(x, row * cols + 8 * (lane + 64 * p), raw[p]);
     }
-    uint32_t m = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = m > abs_bits(v[p][i]) ? m : abs_bits(v[p][i]);
-    u32x2 codes;
-    if constexpr (GRAN == FP8_SCALE_TENSOR) {
-      codes = cast8<FMT>(v[p], s, m);
-      lane_amax = lane_amax > m ? lane_amax : m;
-    } else if constexpr (GRAN == FP8_SCALE_TILE_1x128) {
-      const bool nan_here = m > 0x7F800000u;
-      m = group_max_u32<16>(m);
-      float sc, sc_inv;
-      current_scale<FMT>(m, sc, sc_inv);
-      codes = cast8<FMT>(v[p], sc, nan_here ? m : 0u);
-      if ((lane & 15) == 0) static_cast<float*>(sinv)[(int64_t)(c >> 4) * rows + row] = sc_inv;
-    } else {
-      const bool nan_here = m > 0x7F800000u;
-      m = group_max_u32<4>(m);
-      uint32_t code;
-      float mult;
-      mx_rule<FMT>(m, code, mult);
-      codes = cast8<FMT>(v[p], mult, nan_here ? m : 0u);
-      if ((lane & 3) == 0) static_cast<uint8_t*>(sinv)[(int64_t)(c >> 2) * rows + row] = (uint8_t)code;
-    }
-    __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + base + 8 * c));
   }
-  // per tensor: the block's amax goes to the slot with one atomic (one per wave measured 3.7x
-  // slower over the whole kernel on 8192 x 4096)
+  for (; grp < g_end; grp += nbx) {
+    const bool live = row < rows;
+    float v[NCH][8];
+    if constexpr (PF) {
+#pragma unroll
+      for (int p = 0; p < NCH; ++p) unpack_chunk<BF16>(raw[p], v[p]);
+    } else if (live) {
+#pragma unroll
+      for (int p = 0; p < NCH; ++p)
+        if (lane + 64 * p < nch) {
+          Chunk<BF16> c1;
+          load_chunk<BF16>(x, row * cols + 8 * (lane + 64 * p), c1);
+          unpack_chunk<BF16>(c1, v[p]);
+        }
+    }
+    // the next row of this wave, in flight while this one is processed
+    const int64_t row_n = (grp + nbx) * kLnRows + wave;
+    if constexpr (PF) {
+      if (grp + nbx < g_end && row_n < rows) {
+#pragma unroll
+        for (int p = 0; p < NCH; ++p)
+          if (lane + 64 * p < nch) load_chunk<BF16>(x, row_n * cols + 8 * (lane + 64 * p), raw[p]);
+      }
+    }
+    if (live) {
+      const int64_t base = row * cols;
+      float sum = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NCH; ++p)
+        if (lane + 64 * p < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sum += v[p][i];
+        }
+      const float mean = wave_sum(sum) / (float)cols;
+      float ssq = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NCH; ++p)
+        if (lane + 64 * p < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            v[p][i] -= mean;
+            ssq += v[p][i] * v[p][i];
+          }
+        }
+      const float rs = 1.0f / sqrtf(wave_sum(ssq) / (float)cols + eps);
+      if (lane == 0) {
+        if (mu_out != nullptr) mu_out[row] = mean;
+        if (rs_out != nullptr) rs_out[row] = rs;
+      }
+#pragma unroll
+      for (int p = 0; p < NCH; ++p) {
+        const int c = lane + 64 * p;
+        // whole 4- and 16-lane groups share the branch: nch is a multiple of 4 (MX) / 16 (1x128)
+        if (c >= nch) continue;
+        const float4 g0 = *reinterpret_cast<const float4*>(g_s + 8 * c);
+        const float4 g1 = *reinterpret_cast<const float4*>(g_s + 8 * c + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        if (beta != nullptr) {
+          const float4 b0 = *reinterpret_cast<const float4*>(b_s + 8 * c);
+          const float4 b1 = *reinterpret_cast<const float4*>(b_s + 8 * c + 4);
+          const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[p][i] = fmaf(v[p][i] * rs, g[i], bb[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] * rs * g[i];
+        }
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = m > abs_bits(v[p][i]) ? m : abs_bits(v[p][i]);
+        u32x2 codes;
+        if constexpr (GRAN == FP8_SCALE_TENSOR) {
+          codes = cast8<FMT>(v[p], s, m);
+          lane_amax = lane_amax > m ? lane_amax : m;
+        } else if constexpr (GRAN == FP8_SCALE_TILE_1x128) {
+          const bool nan_here = m > 0x7F800000u;
+          m = group_max_u32<16>(m);
+          float sc, sc_inv;
+          current_scale<FMT>(m, sc, sc_inv);
+          codes = cast8<FMT>(v[p], sc, nan_here ? m : 0u);
+          if ((lane & 15) == 0) static_cast<float*>(sinv)[(int64_t)(c >> 4) * rows + row] = sc_inv;
+        } else {
+          const bool nan_here = m > 0x7F800000u;
+          m = group_max_u32<4>(m);
+          uint32_t code;
+          float mult;
+          mx_rule<FMT>(m, code, mult);
+          codes = cast8<FMT>(v[p], mult, nan_here ? m : 0u);
+          if ((lane & 3) == 0) static_cast<uint8_t*>(sinv)[(int64_t)(c >> 2) * rows + row] = (uint8_t)code;
+        }
+        __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + base + 8 * c));
+      }
+    }
+    row = row_n;
+  }
+  // per tensor: the block's amax goes to the slot with one atomic (one per wave and row
+  // measured 3.7x slower over the whole kernel on 8192 x 4096)
   if constexpr (GRAN == FP8_SCALE_TENSOR) {
     if (amax_slot != nullptr) {
-      __shared__ uint32_t red[kLnRows];
+      // the gamma / beta area is free once every wave is past the loop (keeps the block
+      // within 64 KB of LDS at 8192 columns)
+      uint32_t* red = reinterpret_cast<uint32_t*>(ln_smem);
       const uint32_t m = wave_max_u32(lane_amax);
+      __syncthreads();
       if (lane == 0) red[wave] = m;
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -154,12 +228,17 @@ template <int FMT, bool BF16, int GRAN>
 static void launch_ln(int nch_blocks, const void* x, const void* gamma, const void* beta, int w_bf16, float eps,
                       int64_t rows, int cols, const float* scale, float* amax_slot, uint8_t* q, void* sinv, float* mu,
                       float* rs, hipStream_t st) {
-  const int row_blocks = (int)((rows + kLnRows - 1) / kLnRows);
-  const dim3 grid(row_blocks), block(64 * kLnRows);
+  const int64_t groups = (rows + kLnRows - 1) / kLnRows;
+  // as many blocks as are resident at once: two per CU up to 2048 columns, one above (the
+  // row's registers allow 2 or 3 waves per SIMD), 32 CUs per XCD
+  const int64_t per_xcd_max = nch_blocks >= 8 ? 32 : 64;
+  const int64_t per_xcd = std::min<int64_t>(per_xcd_max, (groups + 7) / 8);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kLnRows);
+  const size_t lds = 2 * (size_t)cols * sizeof(float);
   uint32_t* slot = reinterpret_cast<uint32_t*>(amax_slot);
-#define SFP8_LN(N)                                                                                              \
-  hipLaunchKernelGGL((ln_quant_kernel<FMT, BF16, GRAN, N>), grid, block, 0, st, x, gamma, beta, w_bf16, eps, rows, \
-                     cols, row_blocks, scale, slot, q, sinv, mu, rs)
+#define SFP8_LN(N)                                                                                                 \
+  hipLaunchKernelGGL((ln_quant_kernel<FMT, BF16, GRAN, N>), grid, block, lds, st, x, gamma, beta, w_bf16, eps, rows, \
+                     cols, groups, scale, slot, q, sinv, mu, rs)
   switch (nch_blocks) {
     case 1: SFP8_LN(1); break;
     case 2: SFP8_LN(2); break;
