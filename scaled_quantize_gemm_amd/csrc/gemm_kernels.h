@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
         }
     }
   });
-  epi.finish(lane);
+  epi.finish(lane, reinterpret_cast<uint32_t*>(smem));
 }
 
 // ------------------------------------------------------------------ large-tile kernel
@@ -609,7 +609,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const uint8_t* __restri
         epi.template out<ACT>(v, gm, gn, N, pair);
       }
   });
-  epi.finish(lane);
+  epi.finish(lane, reinterpret_cast<uint32_t*>(smem));
 }
 
 // ------------------------------------------------------------------ blockwise large-tile kernel
@@ -875,7 +875,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
         epi.template out<ACT>(v, gm, gn, N, quad);
       }
   });
-  epi.finish(lane);
+  epi.finish(lane, reinterpret_cast<uint32_t*>(smem));
 }
 
 template <int MODE, int FA, int FB, int OUT, bool FUSED>
