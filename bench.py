@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mx_8192_traffic.json")
+# the sources each kernel is built from (a counter summary is current only for these)
+GEMM_SOURCES = ["gemm.hip", "gemm_kernels.h", "gemm_epilogue.h", "common.h"]
+QUANT_SOURCES = ["quantize.hip", "quant_rules.h", "common.h"]
 
 
 def _src_hash(*names):
@@ -89,6 +92,75 @@ def cpu_baseline(M=8192, K=8192, numel=1 << 28, rows=3072, stream_sample=1 << 26
             "checksum": float(np.abs(C16).sum())}
 
 
+def _time_us(fn, steps, warmup):
+    """Average launch duration over `steps` back-to-back calls (HIP events on the stream)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def next_rows(sq, workloads, dev, steps, warmup):
+    """LayerNorm + cast of workload 4's X [8192x4096] and its FC1 (8192x14336x4096, per-tensor
+    E4M3) with the plain and the fused epilogues; HBM / MFMA rooflines per kernel."""
+    import torch
+
+    X, W, _ = workloads.w4_inputs()
+    X, W = X.to(dev), W.to(dev)
+    rows, cols = X.shape
+    gen = torch.Generator().manual_seed(4)
+    gamma = (1 + 0.1 * torch.randn(cols, generator=gen)).to(torch.bfloat16).to(dev)
+    beta = (0.1 * torch.randn(cols, generator=gen)).to(torch.bfloat16).to(dev)
+    scale, slot = torch.tensor([448.0 / 5.0], device=dev), torch.zeros(1, device=dev)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    sinv = {sq.FP8_SCALE_TILE_1x128: torch.empty((cols // 128, rows), device=dev),
+            sq.FP8_SCALE_MX_1x32: torch.empty((cols // 32, rows), dtype=torch.uint8, device=dev)}
+    mu, rs = torch.empty(rows, device=dev), torch.empty(rows, device=dev)
+    out = {"metric": "next rows: LayerNorm + cast GB/s, fused-epilogue GEMM TFLOP/s", "steps": steps,
+           "warmup": warmup, "config": {"workload": "workload 4: X [8192x4096] bf16, FC1 8192x14336x4096 E4M3"},
+           "kernels": {}}
+    ln_bytes = rows * cols * 3
+    for name, gran in (("ln_cast_tensor", sq.FP8_SCALE_TENSOR), ("ln_cast_1x128", sq.FP8_SCALE_TILE_1x128),
+                       ("ln_cast_mx", sq.FP8_SCALE_MX_1x32)):
+        us = _time_us(lambda: sq.fp8_layernorm_quantize(X, gamma, beta, 1e-5, sq.FP8_E4M3, gran, scale=scale,
+                                                        amax_slot=slot, q=q, scale_inv_out=sinv.get(gran), mu=mu,
+                                                        rsigma=rs), steps, warmup)
+        out["kernels"][name] = {"us": round(us, 2), "GB/s": round(ln_bytes / us / 1e3, 1),
+                                "hbm_frac": round(ln_bytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+    # FC1 operands under per-tensor scales (amax of the data, as a delayed recipe converges to)
+    sx = torch.tensor([448.0], device=dev) / X.float().abs().max()
+    sw = torch.tensor([448.0], device=dev) / W.float().abs().max()
+    qx, _ = sq.fp8_quantize(X, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sx)
+    qw, _ = sq.fp8_quantize(W, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sw)
+    ix, iw = 1.0 / sx, 1.0 / sw
+    N = W.shape[0]
+    flops = 2.0 * rows * N * cols
+    bias = torch.zeros(N, dtype=torch.bfloat16, device=dev)
+    C16 = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+    H8 = torch.empty((rows, N // 2), dtype=torch.uint8, device=dev)
+    hscale = torch.tensor([448.0 / 4.0], device=dev)
+    cases = {
+        "fc1_plain_bf16": lambda: sq.fp8_gemm(qx, 0, ix, 0, qw, 0, iw, 0, sq.OUT_BF16, C=C16),
+        "fc1_swiglu_e4m3_amax": lambda: sq.fp8_gemm_fused(qx, 0, ix, 0, qw, 0, iw, 0, out_dtype=sq.OUT_E4M3,
+                                                          act=sq.FP8_ACT_SWIGLU, c_scale=hscale, c_amax=slot, C=H8),
+        "fc1_bias_gelu_bf16": lambda: sq.fp8_gemm_fused(qx, 0, ix, 0, qw, 0, iw, 0, out_dtype=sq.OUT_BF16,
+                                                        bias=bias, act=sq.FP8_ACT_GELU, C=C16),
+    }
+    for name, fn in cases.items():
+        us = _time_us(fn, steps, warmup)
+        out["kernels"][name] = {"us": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 1),
+                                "mfma_frac": round(flops / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +169,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device-to-device copy of known size (counter calibration)")
+    ap.add_argument("--next-rows", action="store_true",
+                    help="time the fusions around the path instead (LayerNorm + cast, fused GEMM epilogue) "
+                         "on workload 4's shapes; prints their own JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus N with N > 1 is not supported "
@@ -121,6 +196,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
+        return
+
+    if args.next_rows:
+        print(json.dumps(next_rows(sq, workloads, dev, args.steps, args.warmup)))
         return
 
     M = N = K = 8192
@@ -215,10 +294,10 @@ def main():
                    "in_dtype": "bf16", "out_dtype": "bf16", "stream_numel": NUMEL},
         "roofline": {"kernel": "gemm_mx", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": _traffic("gemm_mx", ["gemm.hip", "common.h"])},
+                     "traffic": _traffic("gemm_mx", GEMM_SOURCES)},
         "roofline_amax_cast": {"kernel": "amax_cast_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
-                               "traffic": _traffic("amax_cast_stream", ["quantize.hip", "common.h"]),
+                               "traffic": _traffic("amax_cast_stream", QUANT_SOURCES),
                                "timing": f"{standalone} back-to-back launches after the timed steps",
                                "in_step_gbs": round(stream_step_gbs, 1)},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in per.items()},
