@@ -162,7 +162,9 @@ struct Epilogue {
       if (threadIdx.x == 0) {
         uint32_t r = red[0];
         for (int i = 1; i < nw; ++i) r = r > red[i] ? r : red[i];
-        if (r != 0u) atomicMax(reinterpret_cast<unsigned int*>(p.c_amax), r);
+        unsigned int* slot = reinterpret_cast<unsigned int*>(p.c_amax);
+        // a plain read first: most blocks do not raise the running maximum
+        if (r > __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(slot, r);
       }
     }
   }

@@ -21,7 +21,7 @@
 
 namespace sfp8 {
 
-constexpr int kLnRows = 8;  // waves per block, one row each per step
+constexpr int kLnRows = 4;  // waves per block, one row each per step (small blocks pack the CU)
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -87,12 +87,16 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row addresses in SGPRs
   const int nbx = gridDim.x >> 3, xcd = blockIdx.x & 7;
   const int64_t g_end = groups * (xcd + 1) / 8;
   const int nch = cols >> 3;
   float s = 1.0f;
   if constexpr (GRAN == FP8_SCALE_TENSOR) s = *scale_p;
+  // this lane's scale column: run (lane + 64p) / 16 of 1x128 tiles, (lane + 64p) / 4 of MX
+  float* const sinv_tile = static_cast<float*>(sinv) + (int64_t)(lane >> 4) * rows;
+  uint8_t* const sinv_mx = static_cast<uint8_t*>(sinv) + (int64_t)(lane >> 2) * rows;
   uint32_t lane_amax = 0u;
 
   // the next row is prefetched when its raw chunks fit beside the current row's values (rows
@@ -157,6 +161,11 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
         if (mu_out != nullptr) mu_out[row] = mean;
         if (rs_out != nullptr) rs_out[row] = rs;
       }
+      // A NaN or inf anywhere in the row makes mean or rs non-finite, and then every y of the
+      // row is NaN; otherwise no y is NaN.  So NaN handling (unsigned amax over |y| bits, code
+      // rewrite) is a per-row, wave-uniform branch, and finite rows take the float max with an
+      // abs modifier and no rewrite.
+      const bool nan_row = __builtin_amdgcn_readfirstlane(__builtin_isfinite(mean) && __builtin_isfinite(rs) ? 0 : 1);
 #pragma unroll
       for (int p = 0; p < NCH; ++p) {
         const int c = lane + 64 * p;
@@ -175,29 +184,34 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] * rs * g[i];
         }
-        uint32_t m = 0u;
+        uint32_t m;
+        if (nan_row) {
+          m = 0u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = m > abs_bits(v[p][i]) ? m : abs_bits(v[p][i]);
-        u32x2 codes;
+          for (int i = 0; i < 8; ++i) m = m > abs_bits(v[p][i]) ? m : abs_bits(v[p][i]);
+        } else {
+          float mf = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[p][i]));
+          m = __float_as_uint(mf);
+        }
+        const uint32_t own = m;  // this lane's |y| bits max (NaN bits only on NaN rows)
+        float sc = s;
         if constexpr (GRAN == FP8_SCALE_TENSOR) {
-          codes = cast8<FMT>(v[p], s, m);
           lane_amax = lane_amax > m ? lane_amax : m;
         } else if constexpr (GRAN == FP8_SCALE_TILE_1x128) {
-          const bool nan_here = m > 0x7F800000u;
           m = group_max_u32<16>(m);
-          float sc, sc_inv;
+          float sc_inv;
           current_scale<FMT>(m, sc, sc_inv);
-          codes = cast8<FMT>(v[p], sc, nan_here ? m : 0u);
-          if ((lane & 15) == 0) static_cast<float*>(sinv)[(int64_t)(c >> 4) * rows + row] = sc_inv;
+          if ((lane & 15) == 0) sinv_tile[(int64_t)(4 * p) * rows + row] = sc_inv;
         } else {
-          const bool nan_here = m > 0x7F800000u;
           m = group_max_u32<4>(m);
           uint32_t code;
-          float mult;
-          mx_rule<FMT>(m, code, mult);
-          codes = cast8<FMT>(v[p], mult, nan_here ? m : 0u);
-          if ((lane & 3) == 0) static_cast<uint8_t*>(sinv)[(int64_t)(c >> 2) * rows + row] = (uint8_t)code;
+          mx_rule<FMT>(m, code, sc);
+          if ((lane & 3) == 0) sinv_mx[(int64_t)(16 * p) * rows + row] = (uint8_t)code;
         }
+        u32x2 codes = cast8<FMT>(v[p], sc, 0u);
+        if (nan_row) codes = cast8<FMT>(v[p], sc, own);
         __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + base + 8 * c));
       }
     }
@@ -218,7 +232,8 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
         uint32_t r = red[0];
 #pragma unroll
         for (int i = 1; i < kLnRows; ++i) r = r > red[i] ? r : red[i];
-        if (r != 0u) atomicMax(amax_slot, r);
+        // a plain read first: the blocks end together, and most do not raise the maximum
+        if (r > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_slot, r);
       }
     }
   }
@@ -229,16 +244,27 @@ static void launch_ln(int nch_blocks, const void* x, const void* gamma, const vo
                       int64_t rows, int cols, const float* scale, float* amax_slot, uint8_t* q, void* sinv, float* mu,
                       float* rs, hipStream_t st) {
   const int64_t groups = (rows + kLnRows - 1) / kLnRows;
-  // as many blocks as are resident at once: two per CU up to 2048 columns, one above (the
-  // row's registers allow 2 or 3 waves per SIMD), 32 CUs per XCD
-  const int64_t per_xcd_max = nch_blocks >= 8 ? 32 : 64;
-  const int64_t per_xcd = std::min<int64_t>(per_xcd_max, (groups + 7) / 8);
-  const dim3 grid((unsigned)(8 * per_xcd)), block(64 * kLnRows);
   const size_t lds = 2 * (size_t)cols * sizeof(float);
   uint32_t* slot = reinterpret_cast<uint32_t*>(amax_slot);
-#define SFP8_LN(N)                                                                                                 \
-  hipLaunchKernelGGL((ln_quant_kernel<FMT, BF16, GRAN, N>), grid, block, lds, st, x, gamma, beta, w_bf16, eps, rows, \
-                     cols, groups, scale, slot, q, sinv, mu, rs)
+  // as many blocks as are resident at once (registers and LDS decide: 2-5 waves per SIMD),
+  // the same number on each of the 8 XCDs
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || n < 8)
+      n = 256;
+    return n;
+  }();
+#define SFP8_LN(N)                                                                                                   \
+  do {                                                                                                               \
+    int per_cu = 0;                                                                                                  \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_quant_kernel<FMT, BF16, GRAN, N>, 64 * kLnRows,     \
+                                                     lds) != hipSuccess || per_cu < 1)                              \
+      per_cu = 1;                                                                                                    \
+    const int64_t per_xcd = std::min<int64_t>((int64_t)per_cu * (cus / 8), (groups + 7) / 8);                        \
+    hipLaunchKernelGGL((ln_quant_kernel<FMT, BF16, GRAN, N>), dim3((unsigned)(8 * per_xcd)), dim3(64 * kLnRows), lds, \
+                       st, x, gamma, beta, w_bf16, eps, rows, cols, groups, scale, slot, q, sinv, mu, rs);          \
+  } while (0)
   switch (nch_blocks) {
     case 1: SFP8_LN(1); break;
     case 2: SFP8_LN(2); break;

@@ -249,3 +249,45 @@ def test_workload4_fc1_swiglu_to_fp8(sq):
     e_y = act_bound(pre, e_pre, SWIGLU)
     check_fp8(np_of(H[torch.from_numpy(r).to(DEV)]), y, e_y, cscale, E4M3, "workload4 fused fc1")
     assert amax.item() >= float((np.abs(y) - e_y).max())
+
+
+@pytest.mark.parametrize("act", [NONE, GELU, SWIGLU])
+def test_fused_k_zero_is_the_activation_of_the_bias(sq, act):
+    """K = 0: the GEMM part is exactly 0, so the output is act(bias) (act(0) without bias)."""
+    announce("fused K = 0", act)
+    M, N = 70, 258
+    A = torch.empty((M, 0), dtype=torch.uint8, device=DEV)
+    B = torch.empty((N, 0), dtype=torch.uint8, device=DEV)
+    bias = np.linspace(-4, 4, N).astype(np.float32)
+    C = sq.fp8_gemm_fused(A, 0, _scal(1.0), 0, B, 0, _scal(1.0), 0, out_dtype=sq.OUT_F32, bias=_t(bias), act=act)
+    torch.cuda.synchronize()
+    pre, y = oe.epilogue_ref(np.zeros((M, N)), bias, act)
+    e = act_bound(pre, np.zeros_like(pre), act)
+    check_values(np_of(C), y, e, False, f"K=0 act{act}")
+
+
+def test_fp8_weight_stored_once(sq):
+    """Quantize-once FP8 weights (the tutorial's fp8_model_init idea): the weight's codes and
+    scale_inv are made once and reused by every step's GEMM, with fresh activations each step;
+    each step equals the oracle on the stored codes."""
+    import workloads
+
+    W = workloads.w1_weight()
+    sw = np.float32(448.0 / float(W.abs().max()))
+    qw, _ = sq.fp8_quantize(W.to(DEV), 0, sq.FP8_SCALE_TENSOR, scale=_scal(sw))
+    torch.cuda.synchronize()
+    stored = np_of(qw).copy()
+    for step in range(3):
+        announce("stored FP8 weight, step", step)
+        X = workloads.w1_input(step)
+        sx = np.float32(448.0 / float(X.abs().max()))
+        qx, _ = sq.fp8_quantize(X.to(DEV), 0, sq.FP8_SCALE_TENSOR, scale=_scal(sx))
+        Y = sq.fp8_gemm_fused(qx, 0, _scal(np.float32(1) / sx), 0, qw, 0, _scal(np.float32(1) / sw), 0,
+                              out_dtype=sq.OUT_F32)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_of(qw), stored), "stored weight codes changed"
+        oqx = oq.quantize_tensor(X.numpy(), sx, 0)[0]
+        oqw = oq.quantize_tensor(W.numpy(), sw, 0)[0]
+        assert np.array_equal(stored, oqw)
+        Cr, S, G = og.gemm_ref(oqx, 0, np.float32(1) / sx, og.TENSOR, oqw, 0, np.float32(1) / sw, og.TENSOR)
+        check_values(np_of(Y), Cr, gemm_bound(S, G, 256, "tensor", False, Cr, Cr), False, f"stored W step {step}")

@@ -220,3 +220,10 @@ def test_workload4_input_layernorm(sq):
     r = np.sort(rng.choice(8192, 64, replace=False))
     for gran in (oln.TENSOR, oln.TILE_1x128):
         check_ln(sq, X, g, b, 0, gran, f"workload4 LN gran{gran}", rows=r, scale=448.0 / 5.0)
+
+
+def test_layernorm_mx_rows_not_multiple_of_group(sq):
+    """MX at 1000 rows (not a multiple of the 8-row groups) and bf16 gamma without beta."""
+    rng = np.random.default_rng(13)
+    x, g, _ = _inputs(rng, 1000, 1536, torch.bfloat16)
+    check_ln(sq, x, g, None, 1, oln.MX_1x32, "mx 1000x1536 no beta")
