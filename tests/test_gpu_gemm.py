@@ -145,7 +145,7 @@ def test_mx_gemm(sq, out, mnk):
     check_gemm(np_of(C), Cr, S, G, K, "mx", out == 1, f"mx {mnk} out{out}")
 
 
-# Shapes with >= 128 tiles of 256 x 256 run on the large-tile kernel: ragged edges, K steps
+# Shapes with many 256 x 256 tiles on the large-tile kernel: ragged edges, K steps
 # fewer than the pipeline depth and not a multiple of it.
 BIG_CASES = [(2048, 4096, 128), (2148, 4036, 384), (4096, 2304, 1152), (2052, 4100, 256)]
 
@@ -179,7 +179,7 @@ def test_large_tile_kernel(sq, mnk, mode):
         check_gemm(np_of(C)[r], Cr, S, G, K, "mx", False, f"large mx {mnk}")
 
 
-# Blockwise shapes with >= 128 tiles of 256 x 128 run on the large-tile blockwise kernel:
+# Blockwise shapes with many 256 x 128 tiles on the large-tile blockwise kernel:
 # ragged M and N (N odd takes the unpaired epilogue), K steps fewer than and not a multiple
 # of the pipeline depth.
 BIG_BLOCK_CASES = [(2085, 4100, 384), (2048, 4097, 1152), (4096, 2304, 256), (1300, 3000, 128)]
