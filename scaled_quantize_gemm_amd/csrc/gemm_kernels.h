@@ -649,14 +649,17 @@ __device__ __forceinline__ int blk_row_of(int q) { return (q & ~63) + 4 * (q & 1
 // position of 16-byte chunk c in 128-byte LDS row q (the small-tile kernel's swizzle)
 __device__ __forceinline__ int blk_pos(int q, int c) { return c ^ (((q >> 1) ^ ((q & 1) << 2)) & 7); }
 
-// MODE: MODE_BLOCK (B scales per 128x128 block: one value per stage) or MODE_TILE2 (B scales
-// per 1x128 run along K: one per column per stage, [K/128][N])
+// MODE: MODE_BLOCK (B scales per 128x128 block: one value per stage), MODE_TILE2 (B scales
+// per 1x128 run along K: one per column per stage, [K/128][N]) or MODE_TENSOR (no scale loads;
+// the MFMAs accumulate straight into acc and the epilogue multiplies by sa * sb: the 256 x 128
+// tile gives small per-tensor problems twice the tiles of the 256 x 256 kernel)
 template <int MODE, int FA, int FB, int OUT, bool FUSED>
 __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                           const float* __restrict__ sa_p,
                                                           const float* __restrict__ sb_p, const EpiParams ep, int M,
                                                           int N, int K, int tiles_m, int tiles_n) {
   constexpr int STAGE = BLK_STAGE, NST = BLK_NST, D = NST - 1, U = NST;
+  constexpr bool TENSOR = MODE == MODE_TENSOR;
   static_assert(NST * STAGE <= 160 * 1024, "LDS ring must fit the 160 KB of a CU");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
 
@@ -689,9 +692,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   }
   const int nkb = nk;
   const bool s_is_a = wave < 4;
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t s_voff;
-  if (s_is_a) {
+  __amdgpu_buffer_rsrc_t rs = ra;
+  uint32_t s_voff = 0;
+  if constexpr (TENSOR) {
+  } else if (s_is_a) {
     const uint64_t bytes = ((uint64_t)nkb * M - m0) * 4;
     rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sa_p + m0), (short)0,
                                            (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
@@ -718,11 +722,13 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     for (int i = 0; i < 6; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wave * 6 + i < 32 ? ra : rb, (lds_ptr_t)(buf + (wave * 6 + i) * 1024), 16,
                                                od[i], ks * BLK_BK, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(buf + s_lds), 4, s_voff, ks * s_step, 0, 0);
+    if constexpr (!TENSOR)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(buf + s_lds), 4, s_voff, ks * s_step, 0, 0);
   };
-  // wait until at most `later` stages of this wave's loads (7 per stage) are in flight
+  // wait until at most `later` stages of this wave's loads (7 per stage, 6 per tensor) are in
+  // flight
   auto wait_stage = [&](int later) {
-    if (later >= 1) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    if (later >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(TENSOR ? 6 : 7) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
@@ -764,6 +770,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     fb[1] = pack(ds_read16<1 * 2048>(b_lo[ST]), ds_read16<1 * 2048>(b_hi[ST]));
     fb[2] = pack(ds_read16<2 * 2048>(b_lo[ST]), ds_read16<2 * 2048>(b_hi[ST]));
     fb[3] = pack(ds_read16<3 * 2048>(b_lo[ST]), ds_read16<3 * 2048>(b_hi[ST]));
+    if constexpr (TENSOR) return;
     const u32x4 s0 = ds_read16<0>(s_a[ST]), s1 = ds_read16<16>(s_a[ST]), s2 = ds_read16<32>(s_a[ST]),
                 s3 = ds_read16<48>(s_a[ST]);
     const u32x4 sv[4] = {s0, s1, s2, s3};
@@ -787,6 +794,15 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   // 16 MFMAs, each partial folded into its accumulators two MFMAs later:
   // acc[i][j][jj] += p * (sa[row 16g + 4jj + i] * sb[block] or sb[column 4r + j])
   auto compute = [&]() {
+    if constexpr (TENSOR) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t >> 2], fb[t & 3], acc[t >> 2][t & 3],
+                                                                               FA, FB, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     float sab[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sab[e] = MODE == MODE_BLOCK ? fsa[e] * fsb[0] : fsa[e];
@@ -857,6 +873,8 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 
   // ---- epilogue: acc[i][j][jj] is tile row slab + 16g + 4jj + i, column slab + 4r + j
   Epilogue<OUT, FUSED> epi(ep);
+  float scale = 1.0f;
+  if constexpr (TENSOR) scale = sa_p[0] * sb_p[0];
   const int gn = n0 + slab_b + 4 * r;
   const bool quad = (N & 3) == 0 && gn + 3 < N;  // all four columns present, store aligned
   float b[4];
@@ -870,6 +888,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
         const int gm = m0 + slab_a + 16 * g + 4 * jj + i;
         if (gm >= M) continue;
         float v[4] = {acc[i][0][jj], acc[i][1][jj], acc[i][2][jj], acc[i][3][jj]};
+        if constexpr (TENSOR) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] *= scale;
+        }
         epi.pre(v, b);
         epi.aux(v, gm, gn, N, quad);
         epi.template out<ACT>(v, gm, gn, N, quad);
@@ -881,6 +903,18 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 template <int MODE, int FA, int FB, int OUT, bool FUSED>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, const EpiParams& ep, int M,
                        int N, int K, hipStream_t st, const char* what) {
+  if constexpr (MODE == MODE_TENSOR) {
+    // fewer 256 x 256 tiles than CUs: the 256 x 128 tiles of the blockwise kernel keep twice
+    // as many CUs busy (workload 2's per-tensor GEMMs 1.5x faster); from one full wave of
+    // tiles on, the 256 x 256 kernel reads less per FLOP and wins
+    const int64_t big_tiles = (int64_t)((M + BIG_BM - 1) / BIG_BM) * ((N + BIG_BN - 1) / BIG_BN);
+    if (big_tiles < 256 && 256ll * K < (1ll << 32)) {
+      const int tiles_m = (M + BLK_BM - 1) / BLK_BM, tiles_n = (N + BLK_BN - 1) / BLK_BN;
+      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+                         static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m, tiles_n);
+      return check_launch(what);
+    }
+  }
   if constexpr (MODE == MODE_TENSOR || MODE == MODE_MX) {
     const int tiles_m = (M + BIG_BM - 1) / BIG_BM, tiles_n = (N + BIG_BN - 1) / BIG_BN;
     // every size it supports: even with a few tiles (e.g. 2048 x 2304 x 768, 72 tiles) it beats
