@@ -152,3 +152,14 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus 2 exits non-zero with a message, before touching a GPU."""
+    import subprocess
+    import sys
+
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert p.returncode != 0
+    assert "one GPU" in p.stderr
