@@ -203,3 +203,54 @@ def test_large_tile_blockwise(sq, mnk, out):
     r[-1] = M - 1
     Cr, S, G = og.gemm_ref(A, 0, sa, og.TILE_1x128, B, 0, sb, og.BLOCK_128x128, rows=r)
     check_gemm(np_of(C)[r], Cr, S, G, K, "block", out == 1, f"large blockwise {mnk} out{out}")
+
+
+@pytest.mark.parametrize("mode", ["tensor", "mx", "block"])
+def test_long_k(sq, mode):
+    """K = 65536 (512 promotion blocks, 1024 K steps of the 256x256 kernel) at a small output."""
+    M, N, K = 256, 260 if mode != "mx" else 256, 65536
+    announce("long K", mode, (M, N, K))
+    rng = np.random.default_rng(65536 + len(mode))
+    if mode == "tensor":
+        A, B = _codes(rng, (M, K), 0, True), _codes(rng, (N, K), 0, True)
+        sa, sb = np.float32(0.01), np.float32(0.02)
+        C = sq.fp8_gemm(_t(A), 0, _scal(sa), 0, _t(B), 0, _scal(sb), 0, sq.OUT_F32)
+        torch.cuda.synchronize()
+        Cr, S, G = og.gemm_ref(A, 0, sa, og.TENSOR, B, 0, sb, og.TENSOR)
+    elif mode == "mx":
+        x = rng.standard_normal((M, K)).astype(np.float32)
+        w = rng.standard_normal((N, K)).astype(np.float32)
+        A, ea = oq.quantize_mx_1x32(x, 0)
+        B, eb = oq.quantize_mx_1x32(w, 0)
+        C = sq.fp8_gemm(_t(A), 0, _t(ea.T), sq.FP8_SCALE_MX_1x32, _t(B), 0, _t(eb.T), sq.FP8_SCALE_MX_1x32,
+                        sq.OUT_F32)
+        torch.cuda.synchronize()
+        Cr, S, G = og.gemm_ref(A, 0, ea, og.MX_1x32, B, 0, eb, og.MX_1x32)
+    else:
+        x = rng.standard_normal((M, K)).astype(np.float32)
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        A, sa = oq.quantize_tile_1x128(x, 0)
+        B, sb = oq.quantize_block_128x128(w, 0)
+        C = sq.fp8_gemm(_t(A), 0, _t(sa), sq.FP8_SCALE_TILE_1x128, _t(B), 0, _t(sb), sq.FP8_SCALE_BLOCK_128x128,
+                        sq.OUT_F32)
+        torch.cuda.synchronize()
+        Cr, S, G = og.gemm_ref(A, 0, sa, og.TILE_1x128, B, 0, sb, og.BLOCK_128x128)
+    check_gemm(np_of(C), Cr, S, G, K, "block" if mode == "block" else mode, False, f"long K {mode}")
+
+
+@pytest.mark.parametrize("M,N", [(64, 64), (512, 520)])
+def test_all_maximum_codes_sum_exactly(sq, M, N):
+    """Every code 448 (0x7E) or -448 (0xFE): each product is +-200704 = +-49 * 2^12 and any
+    partial sum is a multiple of it below 2^24 * 2^12, so the result is exact: C = 200704 * (K
+    with signs)."""
+    K = 1024
+    announce("all maximum codes", (M, N, K))
+    A = np.full((M, K), 0x7E, np.uint8)
+    A[1::2, :] = 0xFE  # odd rows negative
+    B = np.full((N, K), 0x7E, np.uint8)
+    B[:, : K // 4] = 0xFE  # a quarter of each column negative
+    C = sq.fp8_gemm(_t(A), 0, _scal(1.0), 0, _t(B), 0, _scal(1.0), 0, sq.OUT_F32)
+    torch.cuda.synchronize()
+    row_sign = np.where(np.arange(M) % 2 == 1, -1.0, 1.0)[:, None]
+    want = row_sign * 200704.0 * (K - 2 * (K // 4)) * np.ones((1, N))
+    assert np.array_equal(np_of(C), want.astype(np.float32))
