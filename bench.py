@@ -167,6 +167,18 @@ def next_rows(sq, workloads, dev, steps, warmup):
         "fc1_bias_gelu_bf16": lambda: sq.fp8_gemm_fused(qx, 0, ix, 0, qw, 0, iw, 0, out_dtype=sq.OUT_BF16,
                                                         bias=bias, act=sq.FP8_ACT_GELU, C=C16),
     }
+    # the backward GEMMs of the same layer (hybrid recipe: E5M2 gradients): dgrad dX = dY W
+    # (A = dY, B = W^T), wgrad dW = dY^T X (A = dY^T, B = X^T); operands from the cast-transposes
+    dY = workloads.w4_inputs()[2].to(dev)
+    sd = torch.tensor([57344.0], device=dev) / dY.float().abs().max()
+    _, qwT = sq.fp8_cast_transpose(W, sq.FP8_E4M3, sw)
+    _, qxT = sq.fp8_cast_transpose(X, sq.FP8_E4M3, sx)
+    qd, qdT = sq.fp8_cast_transpose(dY, sq.FP8_E5M2, sd)
+    idy = 1.0 / sd
+    dX = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, cols), dtype=torch.bfloat16, device=dev)
+    cases["fc1_dgrad_e5m2_bf16"] = lambda: sq.fp8_gemm(qd, 1, idy, 0, qwT, 0, iw, 0, sq.OUT_BF16, C=dX)
+    cases["fc1_wgrad_e5m2_bf16"] = lambda: sq.fp8_gemm(qdT, 1, idy, 0, qxT, 0, ix, 0, sq.OUT_BF16, C=dW)
     for name, fn in cases.items():
         us = _time_us(fn, steps, warmup)
         out["kernels"][name] = {"us": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 1),
