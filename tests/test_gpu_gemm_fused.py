@@ -291,3 +291,31 @@ def test_fp8_weight_stored_once(sq):
         assert np.array_equal(stored, oqw)
         Cr, S, G = og.gemm_ref(oqx, 0, np.float32(1) / sx, og.TENSOR, oqw, 0, np.float32(1) / sw, og.TENSOR)
         check_values(np_of(Y), Cr, gemm_bound(S, G, 256, "tensor", False, Cr, Cr), False, f"stored W step {step}")
+
+
+def _random_cases(n=32, seed=2024):
+    """Seeded random shapes over every kernel path: M, N from 1 to 1100 (ragged, odd, tiny),
+    K a multiple of 128 up to 1024, every mode, activation, output type and bias type."""
+    rng = np.random.default_rng(seed)
+    modes = ["tensor", "mx", "block", "tile2"]
+    out = []
+    for i in range(n):
+        mode = modes[i % 4]
+        M = int(rng.integers(1, 1101))
+        N = int(rng.integers(1, 1101))
+        act = int(rng.integers(0, 3))
+        if act == SWIGLU:
+            N += N % 2
+        if mode == "mx" and rng.random() < 0.5:  # half the MX cases on the 256x256 kernel
+            M, N = M + (-M) % 4, N + (-N) % 4
+        K = 128 * int(rng.integers(1, 9))
+        o = int(rng.integers(0, 4))
+        bias_kind = [None, "f32", "bf16"][int(rng.integers(0, 3))]
+        out.append((mode, M, N, K, act, o, bias_kind, bool(rng.random() < 0.3), 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-a{c[4]}o{c[5]}")
+def test_fused_random_shapes(sq, case):
+    mode, M, N, K, act, out, bias_kind, with_aux, seed = case
+    run_case(sq, mode, M, N, K, act, out, bias_kind, with_aux, seed=seed)

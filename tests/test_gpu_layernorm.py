@@ -227,3 +227,26 @@ def test_layernorm_mx_rows_not_multiple_of_group(sq):
     rng = np.random.default_rng(13)
     x, g, _ = _inputs(rng, 1000, 1536, torch.bfloat16)
     check_ln(sq, x, g, None, 1, oln.MX_1x32, "mx 1000x1536 no beta")
+
+
+def _ln_random_cases(n=24, seed=77):
+    """Seeded random LayerNorm shapes: rows 1..3000, cols a multiple of the granularity's run up
+    to 8192, both formats, both input types, with and without beta, offset rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        gran = [oln.TENSOR, oln.TILE_1x128, oln.MX_1x32][i % 3]
+        run = {oln.TENSOR: 8, oln.TILE_1x128: 128, oln.MX_1x32: 32}[gran]
+        cols = run * int(rng.integers(1, 8192 // run + 1))
+        rows = int(rng.integers(1, 3001))
+        out.append((gran, rows, cols, int(rng.integers(0, 2)), bool(rng.random() < 0.5), bool(rng.random() < 0.7),
+                    float(rng.choice([0.0, 3.0, 50.0])), 500 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _ln_random_cases(), ids=lambda c: f"g{c[0]}-{c[1]}x{c[2]}-f{c[3]}")
+def test_layernorm_random_shapes(sq, case):
+    gran, rows, cols, fmt, bf16, with_beta, offset, seed = case
+    rng = np.random.default_rng(seed)
+    x, g, b = _inputs(rng, rows, cols, torch.bfloat16 if bf16 else torch.float32, offset=offset)
+    check_ln(sq, x, g, b if with_beta else None, fmt, gran, f"random {case}", scale=ofp8.FMAX[fmt] / 4.0)
