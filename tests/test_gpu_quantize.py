@@ -187,3 +187,76 @@ def test_quantize_diag_counts(sq, fmt, bf16, n):
     assert_codes_equal(np_of(q).reshape(-1), oq_, "diag codes")
     assert_codes_equal(np_of(q2).reshape(-1), oq_, "diag codes (second call)")
     assert np.isnan(np_of(slot)[0]) == np.isnan(oa)
+
+
+def _quant_random_cases(n=32, seed=31337):
+    """Seeded random shapes for every quantizer and cast-transpose: rows 1..2600, cols a
+    multiple of what the granularity needs, both formats and input types."""
+    rng = np.random.default_rng(seed)
+    kinds = ["tensor", "tile", "block", "mx", "ct", "ct_bw_tile", "ct_bw_block", "tensor"]
+    out = []
+    for i in range(n):
+        kind = kinds[i % len(kinds)]
+        need = {"tensor": 1, "ct": 1, "tile": 128, "block": 128, "mx": 32, "ct_bw_tile": 128, "ct_bw_block": 128}[kind]
+        rows = int(rng.integers(1, 2601))
+        if kind.startswith("ct_bw"):
+            rows = 128 * int(rng.integers(1, 21))
+        cols = need * int(rng.integers(1, 4097 // need + 1)) if need > 1 else int(rng.integers(1, 4097))
+        out.append((kind, rows, cols, int(rng.integers(0, 2)), bool(rng.random() < 0.5), 7000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _quant_random_cases(), ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-f{c[3]}")
+def test_quantizers_random_shapes(sq, case):
+    """Bit-exact codes, scales and amax against the oracle at random shapes."""
+    kind, rows, cols, fmt, bf16, seed = case
+    announce("random quantizer", case)
+    x = _blocky_data(rows, cols, seed=seed)
+    xt = torch.from_numpy(x)
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+    xd, xo = xt.to(DEV), f32_np(xt)
+    with np.errstate(over="ignore"):
+        scale = np.float32(ofp8.FMAX[fmt] / 8.0)
+    if kind == "tensor":
+        slot = torch.zeros(1, device=DEV)
+        q, _ = sq.fp8_quantize(xd, fmt, sq.FP8_SCALE_TENSOR, scale=torch.tensor([scale], device=DEV), amax_slot=slot)
+        torch.cuda.synchronize()
+        oq_, oa = oq.quantize_tensor(xo, scale, fmt)
+        assert_codes_equal(np_of(q).reshape(oq_.shape), oq_, "tensor codes")
+        assert_f32_bits_equal(np_of(slot), np.array([oa], np.float32), "tensor amax")
+    elif kind == "tile":
+        q, s = sq.fp8_quantize(xd, fmt, sq.FP8_SCALE_TILE_1x128)
+        torch.cuda.synchronize()
+        oq_, os_ = oq.quantize_tile_1x128(xo, fmt)
+        assert_codes_equal(np_of(q), oq_, "tile codes")
+        assert_f32_bits_equal(np_of(s), os_, "tile scales")
+    elif kind == "block":
+        q, s = sq.fp8_quantize(xd, fmt, sq.FP8_SCALE_BLOCK_128x128)
+        torch.cuda.synchronize()
+        oq_, os_ = oq.quantize_block_128x128(xo, fmt)
+        assert_codes_equal(np_of(q), oq_, "block codes")
+        assert_f32_bits_equal(np_of(s), os_, "block scales")
+    elif kind == "mx":
+        q, e8 = sq.fp8_quantize(xd, fmt, sq.FP8_SCALE_MX_1x32)
+        torch.cuda.synchronize()
+        oq_, oe = oq.quantize_mx_1x32(xo, fmt)
+        assert_codes_equal(np_of(e8).T, oe, "mx e8m0")
+        assert_codes_equal(np_of(q), oq_, "mx codes")
+    elif kind == "ct":
+        slot = torch.zeros(1, device=DEV)
+        q, qT = sq.fp8_cast_transpose(xd, fmt, torch.tensor([scale], device=DEV), amax_slot=slot)
+        torch.cuda.synchronize()
+        oq_, oqT, oa = oq.cast_transpose(xo, scale, fmt)
+        assert_codes_equal(np_of(q), oq_, "ct codes")
+        assert_codes_equal(np_of(qT), oqT, "ct transposed codes")
+        assert_f32_bits_equal(np_of(slot), np.array([oa], np.float32), "ct amax")
+    else:
+        gran = sq.FP8_SCALE_TILE_1x128 if kind == "ct_bw_tile" else sq.FP8_SCALE_BLOCK_128x128
+        q, s, qT, sT = sq.fp8_cast_transpose_blockwise(xd, fmt, gran)
+        torch.cuda.synchronize()
+        want = oq.cast_transpose_blockwise(xo, fmt, 1 if gran == sq.FP8_SCALE_TILE_1x128 else 2)
+        assert_codes_equal(np_of(q), want[0], "bw codes")
+        assert_f32_bits_equal(np_of(s), want[1], "bw scales")
+        assert_codes_equal(np_of(qT), want[2], "bw transposed codes")
+        assert_f32_bits_equal(np_of(sT), want[3], "bw transposed scales")
