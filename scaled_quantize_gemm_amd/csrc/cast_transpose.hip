@@ -5,7 +5,9 @@
 // operands.  Writing the transposed FP8 copy during the cast keeps every GEMM in the
 // K-contiguous form without a second read of the high-precision tensor.
 //
-// Tile 64 x 64, 256 threads, persistent grid-stride over tiles:
+// Shapes whose sides are multiples of 128 take the 128 x 128 kernel below (its per-tensor mode);
+// the others this one.  Tile 64 x 64, 256 threads, one block per tile (the loop below also
+// serves a capped grid):
 //   phase 1: thread (row r, 8-column chunk) loads 8 elements of rows r and r+32, casts them,
 //            stores the 8 codes to q and to an LDS tile (dword pitch 17 to spread banks);
 //   phase 2: thread (4-column group, 4-row group) reads 4 dwords (4 rows x 4 columns),
@@ -132,15 +134,6 @@ __global__ void __launch_bounds__(256) cast_transpose_kernel(const void* __restr
   }
 }
 
-template <int FMT, bool BF16>
-static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* scale, float* amax_slot, uint8_t* q,
-                     uint8_t* qT, hipStream_t st) {
-  const int64_t ntiles = ((rows + kCtTile - 1) / kCtTile) * ((cols + kCtTile - 1) / kCtTile);
-  const int64_t blocks = ntiles < 4096 ? ntiles : 4096;
-  hipLaunchKernelGGL((cast_transpose_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols,
-                     scale, reinterpret_cast<uint32_t*>(amax_slot), q, qT);
-  return check_launch("fp8_cast_transpose");
-}
 
 // ------------------------------------------------------------------ blockwise cast-transpose
 //
@@ -160,11 +153,20 @@ static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* sca
 
 constexpr int kBwPitch = 33;
 
-template <int FMT, bool BF16, bool TILE>
+// KIND: kBwTile (1x128 runs), kBwBlock (128x128 blocks) or kBwTensor (the caller's per-tensor
+// scale for both copies, the tensor's amax max-reduced into amax_slot: the per-tensor
+// cast-transpose of 128-aligned shapes, whose 128-byte row pieces of q and qT are whole cache
+// lines where the 64 x 64 kernel writes half lines)
+constexpr int kBwTile = 1, kBwBlock = 2, kBwTensor = 0;
+
+template <int FMT, bool BF16, int KIND>
 __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __restrict__ x, int64_t rows,
                                                                 int64_t cols, uint8_t* __restrict__ q,
                                                                 float* __restrict__ q_sinv, uint8_t* __restrict__ qT,
-                                                                float* __restrict__ qT_sinv) {
+                                                                float* __restrict__ qT_sinv,
+                                                                const float* __restrict__ scale_p,
+                                                                uint32_t* __restrict__ amax_slot) {
+  constexpr bool TILE = KIND == kBwTile;
   __shared__ uint32_t lds[128 * kBwPitch];
   __shared__ uint32_t cred[8][128];
   __shared__ float cscale[128];
@@ -187,7 +189,27 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
     }
   }
   float srow[4], scol[8];
-  if constexpr (TILE) {
+  if constexpr (KIND == kBwTensor) {
+    const float sc = *scale_p;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) srow[p] = sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) scol[e] = sc;
+    if (amax_slot != nullptr) {
+      uint32_t mx = m[0];
+#pragma unroll
+      for (int p = 1; p < 4; ++p) mx = mx > m[p] ? mx : m[p];
+      mx = wave_max_u32(mx);
+      if (lane == 0) cred[wave][0] = mx;
+      __syncthreads();
+      if (t == 0) {
+        uint32_t bm = cred[0][0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) bm = bm > cred[w][0] ? bm : cred[w][0];
+        if (bm > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_slot, bm);
+      }
+    }
+  } else if constexpr (TILE) {
     // row runs: the 16 lanes sharing r16
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -294,15 +316,36 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
 }
 
 template <int FMT, bool BF16>
+static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* scale, float* amax_slot, uint8_t* q,
+                     uint8_t* qT, hipStream_t st) {
+  const int64_t ntiles = ((rows + kCtTile - 1) / kCtTile) * ((cols + kCtTile - 1) / kCtTile);
+  // one block per tile: capping the grid (a persistent loop over tiles) measured 1-5% slower
+  // at workload 4's shapes (8192 x 4096, 14336 x 4096, 8192 x 14336 bf16)
+  const int64_t blocks = ntiles < 0x7FFFFFFF ? ntiles : 0x7FFFFFFF;
+  if (rows % 128 == 0 && cols % 128 == 0 && (rows >> 7) * (cols >> 7) < 0x7FFFFFFF) {
+    // 128 x 128 tiles, the blockwise kernel with the per-tensor scale: whole 128-byte lines of q
+    // and qT (8192 x 14336 bf16: 92 us against 132 us on 64 x 64 tiles, inputs and outputs
+    // beyond the last-level cache)
+    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwTensor>), dim3((unsigned)((rows >> 7) * (cols >> 7))),
+                       dim3(512), 0, st, x, rows, cols, q, nullptr, qT, nullptr, scale,
+                       reinterpret_cast<uint32_t*>(amax_slot));
+    return check_launch("fp8_cast_transpose");
+  }
+  hipLaunchKernelGGL((cast_transpose_kernel<FMT, BF16>), dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols,
+                     scale, reinterpret_cast<uint32_t*>(amax_slot), q, qT);
+  return check_launch("fp8_cast_transpose");
+}
+
+template <int FMT, bool BF16>
 static int launch_ct_bw(const void* x, int64_t rows, int64_t cols, int gran, uint8_t* q, float* q_sinv, uint8_t* qT,
                         float* qT_sinv, hipStream_t st) {
   const int64_t blocks = (rows >> 7) * (cols >> 7);
   if (gran == FP8_SCALE_TILE_1x128)
-    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, true>), dim3((unsigned)blocks), dim3(512), 0, st, x, rows,
-                       cols, q, q_sinv, qT, qT_sinv);
+    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwTile>), dim3((unsigned)blocks), dim3(512), 0, st, x,
+                       rows, cols, q, q_sinv, qT, qT_sinv, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, false>), dim3((unsigned)blocks), dim3(512), 0, st, x,
-                       rows, cols, q, q_sinv, qT, qT_sinv);
+    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwBlock>), dim3((unsigned)blocks), dim3(512), 0, st, x,
+                       rows, cols, q, q_sinv, qT, qT_sinv, nullptr, nullptr);
   return check_launch("fp8_cast_transpose_blockwise");
 }
 

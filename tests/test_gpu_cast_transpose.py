@@ -17,7 +17,9 @@ def sq():
     return m
 
 
-SHAPES = [(1, 1), (64, 64), (128, 192), (100, 37), (3, 1000), (200, 136), (257, 130), (2048, 768), (64, 2304)]
+# 128-aligned shapes take the 128 x 128 kernel, the others the 64 x 64 kernel
+SHAPES = [(1, 1), (64, 64), (128, 192), (100, 37), (3, 1000), (200, 136), (257, 130), (2048, 768), (64, 2304),
+          (128, 128), (256, 384), (384, 128)]
 
 
 @pytest.mark.parametrize("fmt", [ofp8.E4M3, ofp8.E5M2])
@@ -44,9 +46,10 @@ def test_cast_transpose_matches_oracle(sq, fmt, bf16, shape):
     assert_f32_bits_equal(np_of(slot), [oa], "amax")
 
 
-def test_cast_transpose_nan_propagates(sq):
-    announce("cast_transpose NaN")
-    x = np.ones((64, 64), np.float32)
+@pytest.mark.parametrize("shape", [(64, 64), (256, 256)])
+def test_cast_transpose_nan_propagates(sq, shape):
+    announce("cast_transpose NaN", shape)
+    x = np.ones(shape, np.float32)
     x[10, 20] = np.nan
     x[11, 21] = -np.nan
     s = torch.ones(1, device=DEV)
