@@ -300,6 +300,33 @@ def main():
     torch.cuda.synchronize()
     stream_alone_ms = e0.elapsed_time(e1) / standalone
 
+    # the cast-transpose of the hybrid backward on workload 4's gradient dY [8192 x 14336] bf16 ->
+    # E5M2 q and qT (per-tensor delayed scale, amax into its slot): 470 MB per launch, beyond the
+    # 256 MB last-level cache, and still rotated over two copies (the same buffers every launch
+    # measured 17% faster: part of them stays cached).  Beside it, a device-to-device copy of the
+    # same 235 MB (read as much as written, the cast-transpose's 1:1 mix): the rate HBM gives that mix
+    dY = workloads.w4_inputs()[2].to(dev)
+    dYs = [dY, dY.clone()]
+    ct_rows, ct_cols = dY.shape
+    ct_state = sq.DelayedScalingState([sq.FP8_E5M2], history_len=16, device=str(dev))
+    ct_scale, ct_slot, _ = ct_state.slot(0)
+    ct_scale.fill_(57344.0 / 5e-4)
+    cq = [torch.empty((ct_rows, ct_cols), dtype=torch.uint8, device=dev) for _ in dYs]
+    cqT = [torch.empty((ct_cols, ct_rows), dtype=torch.uint8, device=dev) for _ in dYs]
+    turn = [0]
+
+    def cast_transpose():
+        i = turn[0] = (turn[0] + 1) % len(dYs)
+        sq.fp8_cast_transpose(dYs[i], sq.FP8_E5M2, ct_scale, amax_slot=ct_slot, q=cq[i], qT=cqT[i])
+
+    ct_us = _time_us(cast_transpose, standalone, 5)
+    ct_bytes = ct_rows * ct_cols * (2 + 1 + 1)
+    ct_gbs = ct_bytes / ct_us / 1e3
+    cp_dst = torch.empty_like(dY)
+    cp_us = _time_us(lambda: cp_dst.copy_(dYs[1]), standalone, 5)
+    cp_gbs = 2 * dY.numel() * 2 / cp_us / 1e3
+    del dY, dYs, cq, cqT, cp_dst
+
     gemm_flops = 2.0 * M * N * K
     stream_bytes = NUMEL * (2 + 1)  # bf16 read + E4M3 write (amax is a scalar)
     mxq_bytes = M * K * (2 + 1) + M * (K // 32)
@@ -333,6 +360,15 @@ def main():
                                "traffic": _traffic("amax_cast_stream", QUANT_SOURCES),
                                "timing": f"{standalone} back-to-back launches after the timed steps",
                                "in_step_gbs": round(stream_step_gbs, 1)},
+        "roofline_cast_transpose": {"kernel": "cast_transpose_e5m2", "bound": "hbm", "achieved": round(ct_gbs, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ct_gbs / PEAK_HBM_GBS, 4),
+                                    "us": round(ct_us, 2),
+                                    "config": f"workload 4 dY [{ct_rows}x{ct_cols}] bf16 -> E5M2 q + qT, per-tensor "
+                                              "delayed scale + amax",
+                                    "timing": f"{standalone} back-to-back launches after the timed steps, "
+                                              "input and outputs rotated over 2 copies",
+                                    "copy_gbs": round(cp_gbs, 1),
+                                    "copy": "device-to-device copy of the same bf16 tensor (read + written bytes)"},
         "kernels_us": {n: round(per[n] * 1e3, 2) for n in names},
         "kernels_timing": "gemm_mx: HIP events in the timed steps; the others: a second pass of the same steps "
                           "with every call bracketed",

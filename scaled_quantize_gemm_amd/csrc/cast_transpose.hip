@@ -171,7 +171,23 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
   __shared__ uint32_t cred[8][128];
   __shared__ float cscale[128];
   const int64_t nkb = cols >> 7, nrb = rows >> 7;
-  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
+  // tile order.  Blockwise modes: row-band major (a band's blocks read whole source rows).
+  // Per tensor: bands of 8 tile rows walked column by column, so that the blocks in flight
+  // together write 1 KB runs of each qT row instead of 128-byte pieces spread over all of
+  // them (workload 4's dY 8192 x 14336: 99 -> 91 us, the rate of a device-to-device copy with
+  // the same read:write mix; 64-row bands helped dY more and X, W less)
+  int64_t rb, kb;
+  if constexpr (KIND == kBwTensor) {
+    constexpr int64_t SR = 8;
+    const int64_t band = blockIdx.x / (SR * nkb), first = band * SR;
+    const int64_t h = nrb - first < SR ? nrb - first : SR;
+    const int64_t in = blockIdx.x - band * SR * nkb;
+    rb = first + in % h;
+    kb = in / h;
+  } else {
+    rb = blockIdx.x / nkb;
+    kb = blockIdx.x - rb * nkb;
+  }
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r16 = t >> 4, cg = t & 15;
   const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
