@@ -15,31 +15,12 @@
 //            (4 consecutive source rows) to each of 4 rows of qT; 16 lanes cover 64
 //            contiguous bytes of a qT row.
 // Tiles that are partial or whose rows are not 16-byte aligned take an element-wise path.
-#include "common.h"
+#include "quant_rules.h"
 
 namespace sfp8 {
 
 constexpr int kCtTile = 64;
 constexpr int kCtPitch = 17;  // dwords per LDS row (16 + 1 pad)
-
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t elem, float (&v)[8]) {
-  if constexpr (BF16) {
-    u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem));
-    uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + elem);
-    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
-  }
-}
 
 template <bool BF16>
 __device__ __forceinline__ float ld1(const void* __restrict__ base, int64_t i) {
@@ -158,6 +139,7 @@ constexpr int kBwPitch = 33;
 // cast-transpose of 128-aligned shapes, whose 128-byte row pieces of q and qT are whole cache
 // lines where the 64 x 64 kernel writes half lines)
 constexpr int kBwTile = 1, kBwBlock = 2, kBwTensor = 0;
+constexpr size_t kCtTensorLdsPad = 20 * 1024;
 
 template <int FMT, bool BF16, int KIND>
 __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __restrict__ x, int64_t rows,
@@ -191,19 +173,14 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r16 = t >> 4, cg = t & 15;
   const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
-  float v[4][8];
+  // the tile stays as loaded (packed bf16: 16 VGPRs) until the cast widens it: widened at the
+  // load, the kernel held 70 VGPRs (3 blocks per CU)
+  Raw8<BF16> raw[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) load8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols, v[p]);
+  for (int p = 0; p < 4; ++p) raw[p] = load_raw8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols);
   uint32_t m[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    m[p] = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t a = abs_bits(v[p][e]);
-      m[p] = m[p] > a ? m[p] : a;
-    }
-  }
+  for (int p = 0; p < 4; ++p) m[p] = raw_amax_bits<BF16>(raw[p]);
   float srow[4], scol[8];
   if constexpr (KIND == kBwTensor) {
     const float sc = *scale_p;
@@ -240,7 +217,7 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
       uint32_t c = 0;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t a = abs_bits(v[p][e]);
+        const uint32_t a = raw_abs_bits<BF16>(raw[p], e);
         c = c > a ? c : a;
       }
       uint32_t o = (uint32_t)__shfl_xor((int)c, 16, 64);
@@ -288,17 +265,21 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
   }
   // q with the row scales; the qT codes (column scales) into the LDS tile
 #pragma unroll
+  for (int p = 0; p < 4; ++p) opaque_raw8<BF16>(raw[p]);
+#pragma unroll
   for (int p = 0; p < 4; ++p) {
     const float sr = srow[p];
-    uint32_t w0 = cvt4<FMT>(v[p][0] * sr, v[p][1] * sr, v[p][2] * sr, v[p][3] * sr);
-    uint32_t w1 = cvt4<FMT>(v[p][4] * sr, v[p][5] * sr, v[p][6] * sr, v[p][7] * sr);
-    uint32_t c0 = cvt4<FMT>(v[p][0] * scol[0], v[p][1] * scol[1], v[p][2] * scol[2], v[p][3] * scol[3]);
-    uint32_t c1 = cvt4<FMT>(v[p][4] * scol[4], v[p][5] * scol[5], v[p][6] * scol[6], v[p][7] * scol[7]);
+    float v[8];
+    widen8<BF16>(raw[p], v);
+    uint32_t w0 = cvt4<FMT>(v[0] * sr, v[1] * sr, v[2] * sr, v[3] * sr);
+    uint32_t w1 = cvt4<FMT>(v[4] * sr, v[5] * sr, v[6] * sr, v[7] * sr);
+    uint32_t c0 = cvt4<FMT>(v[0] * scol[0], v[1] * scol[1], v[2] * scol[2], v[3] * scol[3]);
+    uint32_t c1 = cvt4<FMT>(v[4] * scol[4], v[5] * scol[5], v[6] * scol[6], v[7] * scol[7]);
     if (m[p] > 0x7F800000u) {
-      w0 = patch_nan4(w0, &v[p][0]);
-      w1 = patch_nan4(w1, &v[p][4]);
-      c0 = patch_nan4(c0, &v[p][0]);
-      c1 = patch_nan4(c1, &v[p][4]);
+      w0 = patch_nan4(w0, &v[0]);
+      w1 = patch_nan4(w1, &v[4]);
+      c0 = patch_nan4(c0, &v[0]);
+      c1 = patch_nan4(c1, &v[4]);
     }
     const u32x2 w = {w0, w1};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(q + base + (int64_t)(r16 + 32 * p) * cols));
@@ -342,8 +323,10 @@ static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* sca
     // 128 x 128 tiles, the blockwise kernel with the per-tensor scale: whole 128-byte lines of q
     // and qT (8192 x 14336 bf16: 92 us against 132 us on 64 x 64 tiles, inputs and outputs
     // beyond the last-level cache)
+    // 20 KB of unused dynamic LDS hold residency at 3 blocks per CU (41 KB each of 160 KB): at
+    // the 4 its registers allow, this launch measured 2-5% slower at workload 4's shapes
     hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwTensor>), dim3((unsigned)((rows >> 7) * (cols >> 7))),
-                       dim3(512), 0, st, x, rows, cols, q, nullptr, qT, nullptr, scale,
+                       dim3(512), kCtTensorLdsPad, st, x, rows, cols, q, nullptr, qT, nullptr, scale,
                        reinterpret_cast<uint32_t*>(amax_slot));
     return check_launch("fp8_cast_transpose");
   }

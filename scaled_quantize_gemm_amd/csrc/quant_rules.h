@@ -1,6 +1,6 @@
-// Element rules shared by the quantizers (quantize.hip) and the fused LayerNorm + cast
-// (layernorm.hip): 8-element loads, the scaled saturating cast of 8 values, and the MX
-// (e8m0) scale rule.
+// Element rules shared by the quantizers (quantize.hip), the cast-transposes
+// (cast_transpose.hip) and the fused LayerNorm + cast (layernorm.hip): 8-element loads, packed
+// 8-element runs, the scaled saturating cast of 8 values, and the MX (e8m0) scale rule.
 #pragma once
 
 #include "common.h"
@@ -27,6 +27,104 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t e0, fl
     uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+}
+
+// ------------------------------------------------------------------ packed 8-element runs
+//
+// 8 consecutive elements kept as loaded (bf16: one 16-byte word quad; fp32: two), widened to
+// fp32 only where arithmetic needs them.  A kernel that holds its tile in registers across a
+// barrier needs half the registers for bf16 this way.  The amax works on the bit patterns:
+// |x| as an unsigned integer orders like the value, and NaN sorts above every finite value.
+template <bool BF16>
+struct Raw8 {
+  u32x4 w[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const void* __restrict__ x, int64_t e0) {
+  Raw8<BF16> r;
+  if constexpr (BF16) {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0));
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
+    r.w[0] = __builtin_nontemporal_load(p);
+    r.w[1] = __builtin_nontemporal_load(p + 1);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> zero_raw8() {
+  Raw8<BF16> r;
+#pragma unroll
+  for (int i = 0; i < (BF16 ? 1 : 2); ++i) r.w[i] = u32x4{0u, 0u, 0u, 0u};
+  return r;
+}
+
+// word i: bf16 elements 2i and 2i+1 (i < 4), or fp32 element i (i < 8)
+template <bool BF16>
+__device__ __forceinline__ uint32_t raw_word(const Raw8<BF16>& r, int i) {
+  const u32x4& q = r.w[i >> 2];
+  const int j = i & 3;
+  return j == 0 ? q.x : (j == 1 ? q.y : (j == 2 ? q.z : q.w));
+}
+
+// fp32 bits of |element e|
+template <bool BF16>
+__device__ __forceinline__ uint32_t raw_abs_bits(const Raw8<BF16>& r, int e) {
+  if constexpr (BF16) {
+    const uint32_t w = raw_word<BF16>(r, e >> 1);
+    return (((e & 1) ? (w >> 16) : w) & 0x7FFFu) << 16;
+  } else {
+    return raw_word<BF16>(r, e) & 0x7FFFFFFFu;
+  }
+}
+
+// fp32 bits of the largest |element|
+template <bool BF16>
+__device__ __forceinline__ uint32_t raw_amax_bits(const Raw8<BF16>& r) {
+  uint32_t m = 0;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a = raw_word<BF16>(r, i) & 0x7FFF7FFFu;
+      const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+      m = m > lo ? m : lo;
+      m = m > hi ? m : hi;
+    }
+    return m << 16;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = raw_word<BF16>(r, i) & 0x7FFFFFFFu;
+      m = m > a ? m : a;
+    }
+    return m;
+  }
+}
+
+// the words pass through an empty asm: nothing computed from them before this point (the
+// amax's masked halves equal the widened values' bits) is reused after it, so the compiler
+// cannot keep a widened copy of the tile live across a barrier
+template <bool BF16>
+__device__ __forceinline__ void opaque_raw8(Raw8<BF16>& r) {
+#pragma unroll
+  for (int i = 0; i < (BF16 ? 1 : 2); ++i) asm volatile("" : "+v"(r.w[i]));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen8(const Raw8<BF16>& r, float (&v)[8]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = raw_word<BF16>(r, i);
+      v[2 * i] = bf16_lo(w);
+      v[2 * i + 1] = bf16_hi(w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(raw_word<BF16>(r, i));
   }
 }
 

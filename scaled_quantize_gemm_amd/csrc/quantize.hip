@@ -212,36 +212,11 @@ __global__ void __launch_bounds__(256) quant_tile_kernel(const void* __restrict_
 
 constexpr int kBlockThreads = 512;
 
-template <int FMT, bool BF16>
-__global__ void __launch_bounds__(kBlockThreads) quant_block_kernel(const void* __restrict__ x, int64_t rows,
-                                                                   int64_t cols, uint8_t* __restrict__ q,
-                                                                   float* __restrict__ sinv_out) {
+// the block's amax from each thread's partial maximum `mx` (fp32 bits of |x|): the scale for
+// the cast, with its scale_inv stored by thread 0 at sinv_out[at]
+template <int FMT>
+__device__ __forceinline__ float block_scale(uint32_t mx, int t, float* __restrict__ sinv_out, int64_t at) {
   __shared__ uint32_t red[8];
-  const int64_t nkb = cols >> 7;
-  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
-  const int t = threadIdx.x, r16 = t >> 4, cg = t & 15;
-  const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
-  float v[4][8];
-  uint32_t m[4], mx = 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    if (rb * 128 + r16 + 32 * p < rows) {
-      load8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols, v[p]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    m[p] = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t a = abs_bits(v[p][i]);
-      m[p] = m[p] > a ? m[p] : a;
-    }
-    mx = mx > m[p] ? mx : m[p];
-  }
   mx = wave_max_u32(mx);
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
@@ -250,13 +225,43 @@ __global__ void __launch_bounds__(kBlockThreads) quant_block_kernel(const void* 
   for (int i = 1; i < 8; ++i) bm = bm > red[i] ? bm : red[i];
   float s, s_inv;
   current_scale<FMT>(bm, s, s_inv);
+  if (t == 0) sinv_out[at] = s_inv;
+  return s;
+}
+
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(kBlockThreads) quant_block_kernel(const void* __restrict__ x, int64_t rows,
+                                                                   int64_t cols, uint8_t* __restrict__ q,
+                                                                   float* __restrict__ sinv_out) {
+  const int64_t nkb = cols >> 7;
+  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
+  const int t = threadIdx.x, r16 = t >> 4, cg = t & 15;
+  const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
+  // the 32 values stay as loaded (packed bf16: 16 VGPRs) across the barrier and widen at the
+  // cast: widened at the load, the bf16 kernel held 86 VGPRs (2 blocks per CU, 64 KB of loads
+  // in flight per CU); now 40 (4 blocks)
+  Raw8<BF16> raw[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p)
-    if (rb * 128 + r16 + 32 * p < rows)
-      __builtin_nontemporal_store(cast8<FMT>(v[p], s, m[p]),
+    raw[p] = rb * 128 + r16 + 32 * p < rows ? load_raw8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols)
+                                            : zero_raw8<BF16>();
+  uint32_t m[4], mx = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    m[p] = raw_amax_bits<BF16>(raw[p]);
+    mx = mx > m[p] ? mx : m[p];
+  }
+  const float s = block_scale<FMT>(mx, t, sinv_out, rb * nkb + kb);
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    if (rb * 128 + r16 + 32 * p < rows) {
+      float v[8];
+      widen8<BF16>(raw[p], v);
+      __builtin_nontemporal_store(cast8<FMT>(v, s, m[p]),
                                   reinterpret_cast<u32x2*>(q + base + (int64_t)(r16 + 32 * p) * cols));
-  if (t == 0) sinv_out[rb * nkb + kb] = s_inv;
+    }
 }
+
 
 // ------------------------------------------------------------------ MX 1x32
 //
