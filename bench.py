@@ -39,6 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mx_8192_traffic.json")
 # the sources each kernel is built from (a counter summary is current only for these)
 GEMM_SOURCES = ["gemm.hip", "gemm_kernels.h", "gemm_epilogue.h", "common.h"]
 QUANT_SOURCES = ["quantize.hip", "quant_rules.h", "common.h"]
+CT_SOURCES = ["cast_transpose.hip", "quant_rules.h", "common.h"]
 
 
 def _src_hash(*names):
@@ -186,6 +187,92 @@ def next_rows(sq, workloads, dev, steps, warmup):
     return out
 
 
+def blockwise_rows(sq, workloads, dev, steps, warmup):
+    """Workload 3, blockwise current scaling in E4M3 everywhere: X [4096x7168] bf16 with 1x128
+    scales, W [7168x7168] with 128x128 scales, bf16 out.  The forward's quantizers and GEMM,
+    then the backward's blockwise cast-transposes (X, W, dY [4096x7168]) and its dgrad / wgrad
+    GEMMs; HBM / MFMA rooflines per kernel.  The casts' inputs and outputs rotate over copies
+    that together exceed the 256 MB last-level cache, so that every launch reads and writes HBM."""
+    import torch
+
+    X, W = workloads.w3_inputs()
+    G = workloads.w3_grad()
+    m, k = X.shape
+    n = W.shape[0]
+    TILE, BLOCK = sq.FP8_SCALE_TILE_1x128, sq.FP8_SCALE_BLOCK_128x128
+    out = {"metric": "blockwise rows: 1x128 / 128x128 quantizers and cast-transposes GB/s, blockwise GEMMs TFLOP/s",
+           "steps": steps, "warmup": warmup,
+           "config": {"workload": f"workload 3: X [{m}x{k}] bf16 (0.1% outliers x100), W [{n}x{k}], "
+                                  f"dY [{m}x{n}]; E4M3, 1x128 x 128x128 scales, bf16 out",
+                      "cast_buffers": "inputs and outputs rotated over 4 (X, dY) or 2 (W) copies"},
+           "kernels": {}}
+
+    def rotating(t, copies, fn):
+        """fn(x, i) over `copies` clones of t (each call takes the next)."""
+        xs = [t.to(dev)] + [t.to(dev) for _ in range(copies - 1)]
+        turn = [0]
+
+        def call():
+            i = turn[0] = (turn[0] + 1) % copies
+            fn(xs[i], i)
+
+        return call
+
+    def hbm(name, fn, nbytes):
+        us = _time_us(fn, steps, warmup)
+        out["kernels"][name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+    def mfma(name, fn, flops):
+        us = _time_us(fn, steps, warmup)
+        out["kernels"][name] = {"us": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 1),
+                                "mfma_frac": round(flops / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+
+    # forward quantizers: 3 B per element + 4 B per scale
+    qx = [torch.empty((m, k), dtype=torch.uint8, device=dev) for _ in range(4)]
+    sx = [torch.empty((k // 128, m), device=dev) for _ in range(4)]
+    qw = [torch.empty((n, k), dtype=torch.uint8, device=dev) for _ in range(2)]
+    sw = [torch.empty((n // 128, k // 128), device=dev) for _ in range(2)]
+    hbm("quantize_1x128_X", rotating(X, 4, lambda x, i: sq.fp8_quantize(x, 0, TILE, q=qx[i], scale_inv_out=sx[i])),
+        m * k * 3 + (k // 128) * m * 4)
+    hbm("quantize_128x128_W", rotating(W, 2, lambda x, i: sq.fp8_quantize(x, 0, BLOCK, q=qw[i], scale_inv_out=sw[i])),
+        n * k * 3 + (n // 128) * (k // 128) * 4)
+    C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    mfma("gemm_fwd_1x128_x_128x128", lambda: sq.fp8_gemm(qx[0], 0, sx[0], TILE, qw[0], 0, sw[0], BLOCK, sq.OUT_BF16, C=C),
+         2.0 * m * n * k)
+    del qx, sx, qw, sw, C
+
+    # backward cast-transposes: 4 B per element + both scale arrays
+    def ct_call(rows, cols, gran, copies):
+        if gran == TILE:
+            qs, qts = (cols // 128, rows), (rows // 128, cols)
+        else:
+            qs, qts = (rows // 128, cols // 128), (cols // 128, rows // 128)
+        outs = [(torch.empty((rows, cols), dtype=torch.uint8, device=dev), torch.empty(qs, device=dev),
+                 torch.empty((cols, rows), dtype=torch.uint8, device=dev), torch.empty(qts, device=dev))
+                for _ in range(copies)]
+        nbytes = rows * cols * 4 + 4 * (qs[0] * qs[1] + qts[0] * qts[1])
+        return outs, nbytes, lambda x, i: sq.fp8_cast_transpose_blockwise(x, 0, gran, *outs[i])
+
+    ox, bx, fx = ct_call(m, k, TILE, 4)
+    hbm("cast_transpose_1x128_X", rotating(X, 4, fx), bx)
+    ow, bw, fw = ct_call(n, k, BLOCK, 2)
+    hbm("cast_transpose_128x128_W", rotating(W, 2, fw), bw)
+    og, bg, fg = ct_call(m, n, TILE, 4)
+    hbm("cast_transpose_1x128_dY", rotating(G, 4, fg), bg)
+    # dgrad dX = dY W: A = dY (1x128 runs), B = W^T (its 128x128 blocks); wgrad dW = dY^T X:
+    # A = dY^T, B = X^T, both in 1x128 runs along the tokens
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    mfma("gemm_dgrad_1x128_x_128x128",
+         lambda: sq.fp8_gemm(og[0][0], 0, og[0][1], TILE, ow[0][2], 0, ow[0][3], BLOCK, sq.OUT_BF16, C=dX),
+         2.0 * m * k * n)
+    mfma("gemm_wgrad_1x128_x_1x128",
+         lambda: sq.fp8_gemm(og[0][2], 0, og[0][3], TILE, ox[0][2], 0, ox[0][3], TILE, sq.OUT_BF16, C=dW),
+         2.0 * n * k * m)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +284,9 @@ def main():
     ap.add_argument("--next-rows", action="store_true",
                     help="time the fusions around the path instead (LayerNorm + cast, fused GEMM epilogue) "
                          "on workload 4's shapes; prints their own JSON line")
+    ap.add_argument("--blockwise", action="store_true",
+                    help="time workload 3's blockwise rows instead (1x128 / 128x128 quantizers and "
+                         "cast-transposes, forward / dgrad / wgrad GEMMs); prints their own JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus N with N > 1 is not supported "
@@ -221,6 +311,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
+        return
+
+    if args.blockwise:
+        print(json.dumps(blockwise_rows(sq, workloads, dev, args.steps, args.warmup)))
         return
 
     if args.next_rows:
@@ -362,7 +456,7 @@ def main():
                                "in_step_gbs": round(stream_step_gbs, 1)},
         "roofline_cast_transpose": {"kernel": "cast_transpose_e5m2", "bound": "hbm", "achieved": round(ct_gbs, 1),
                                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ct_gbs / PEAK_HBM_GBS, 4),
-                                    "us": round(ct_us, 2),
+                                    "us": round(ct_us, 2), "traffic": _traffic("cast_transpose_e5m2", CT_SOURCES),
                                     "config": f"workload 4 dY [{ct_rows}x{ct_cols}] bf16 -> E5M2 q + qT, per-tensor "
                                               "delayed scale + amax",
                                     "timing": f"{standalone} back-to-back launches after the timed steps, "
