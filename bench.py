@@ -187,6 +187,87 @@ def next_rows(sq, workloads, dev, steps, warmup):
     return out
 
 
+class MiniGPTStep:
+    """One step of workload 2 (the MiniGPT layer set: tokens 2048, QKV 768 -> 2304, FC1 768 -> 3072,
+    FC2 3072 -> 768), per-tensor delayed scaling, history 16, hybrid formats: per layer the
+    cast-transposes of X and W (E4M3) and dY (E5M2) on their recipe slots, the forward GEMM
+    Y = X W^T (E4M3 x E4M3), dgrad dX = dY W and wgrad dW = dY^T X (E5M2 x E4M3), all bf16 out;
+    then one recipe update for the 9 slots.  Every buffer is allocated up front, so the step can
+    be captured as a graph."""
+
+    def __init__(self, sq, workloads, dev):
+        import torch
+
+        self.sq = sq
+        E4, E5 = sq.FP8_E4M3, sq.FP8_E5M2
+        fmts = []
+        for _ in workloads.MINIGPT_LAYERS:
+            fmts += [E4, E4, E5]
+        self.state = sq.DelayedScalingState(fmts, history_len=16, device=str(dev))
+        self.layers = []
+        self.flops = 0.0
+        for li, (_, k_in, n_out) in enumerate(workloads.MINIGPT_LAYERS):
+            X, W, dY = (t.to(dev) for t in workloads.w2_layer(li, 0))
+            m = X.shape[0]
+            u8 = dict(dtype=torch.uint8, device=dev)
+            bf = dict(dtype=torch.bfloat16, device=dev)
+            L = dict(X=X, W=W, dY=dY, slots=[3 * li, 3 * li + 1, 3 * li + 2],
+                     qx=torch.empty((m, k_in), **u8), qxT=torch.empty((k_in, m), **u8),
+                     qw=torch.empty((n_out, k_in), **u8), qwT=torch.empty((k_in, n_out), **u8),
+                     qd=torch.empty((m, n_out), **u8), qdT=torch.empty((n_out, m), **u8),
+                     Y=torch.empty((m, n_out), **bf), dX=torch.empty((m, k_in), **bf),
+                     dW=torch.empty((n_out, k_in), **bf))
+            self.layers.append(L)
+            self.flops += 3 * 2.0 * m * n_out * k_in
+
+    def __call__(self):
+        sq, st = self.sq, self.state
+        E4, E5 = sq.FP8_E4M3, sq.FP8_E5M2
+        for L in self.layers:
+            (sx, ax, ix), (sw, aw, iw), (sd, ad, idy) = (st.slot(j) for j in L["slots"])
+            sq.fp8_cast_transpose(L["X"], E4, sx, amax_slot=ax, q=L["qx"], qT=L["qxT"])
+            sq.fp8_cast_transpose(L["W"], E4, sw, amax_slot=aw, q=L["qw"], qT=L["qwT"])
+            sq.fp8_cast_transpose(L["dY"], E5, sd, amax_slot=ad, q=L["qd"], qT=L["qdT"])
+            sq.fp8_gemm(L["qx"], E4, ix, 0, L["qw"], E4, iw, 0, sq.OUT_BF16, C=L["Y"])
+            sq.fp8_gemm(L["qd"], E5, idy, 0, L["qwT"], E4, iw, 0, sq.OUT_BF16, C=L["dX"])
+            sq.fp8_gemm(L["qdT"], E5, idy, 0, L["qxT"], E4, ix, 0, sq.OUT_BF16, C=L["dW"])
+        st.update()
+
+    def outputs(self):
+        out = [self.state.amax_history, self.state.scale, self.state.scale_inv]
+        for L in self.layers:
+            out += [L[k] for k in ("qx", "qxT", "qw", "qwT", "qd", "qdT", "Y", "dX", "dW")]
+        return out
+
+
+def minigpt_rows(sq, workloads, dev, steps, warmup):
+    """Workload 2's step, launched call by call and as one captured graph (19 launches of
+    kernels a few microseconds long: launch-bound)."""
+    import torch
+
+    step = MiniGPTStep(sq, workloads, dev)
+    eager_us = _time_us(step, steps, warmup)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    graph_us = _time_us(g.replay, steps, warmup)
+    return {"metric": "MiniGPT layer set step (workload 2): TFLOP/s over the step",
+            "steps": steps, "warmup": warmup,
+            "config": {"workload": "workload 2: tokens 2048; QKV 768->2304, FC1 768->3072, FC2 3072->768; "
+                                   "per-tensor delayed, history 16; fwd E4M3 x E4M3, dgrad / wgrad E5M2 x E4M3; "
+                                   "bf16 out", "gflop_per_step": round(step.flops / 1e9, 2),
+                       "launches_per_step": 19},
+            "eager": {"us_per_step": round(eager_us, 2), "TFLOP/s": round(step.flops / eager_us / 1e6, 1),
+                      "mfma_frac": round(step.flops / eager_us / 1e6 / PEAK_FP8_TFLOPS, 4)},
+            "graph": {"us_per_step": round(graph_us, 2), "TFLOP/s": round(step.flops / graph_us / 1e6, 1),
+                      "mfma_frac": round(step.flops / graph_us / 1e6 / PEAK_FP8_TFLOPS, 4)}}
+
+
 def blockwise_rows(sq, workloads, dev, steps, warmup):
     """Workload 3, blockwise current scaling in E4M3 everywhere: X [4096x7168] bf16 with 1x128
     scales, W [7168x7168] with 128x128 scales, bf16 out.  The forward's quantizers and GEMM,
@@ -284,6 +365,9 @@ def main():
     ap.add_argument("--next-rows", action="store_true",
                     help="time the fusions around the path instead (LayerNorm + cast, fused GEMM epilogue) "
                          "on workload 4's shapes; prints their own JSON line")
+    ap.add_argument("--minigpt", action="store_true",
+                    help="time workload 2's step (MiniGPT layer set, delayed scaling, forward and backward) "
+                         "eager and as a captured graph; prints its own JSON line")
     ap.add_argument("--blockwise", action="store_true",
                     help="time workload 3's blockwise rows instead (1x128 / 128x128 quantizers and "
                          "cast-transposes, forward / dgrad / wgrad GEMMs); prints their own JSON line")
@@ -311,6 +395,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
+        return
+
+    if args.minigpt:
+        print(json.dumps(minigpt_rows(sq, workloads, dev, args.steps, args.warmup)))
         return
 
     if args.blockwise:

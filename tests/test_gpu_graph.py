@@ -1,0 +1,58 @@
+"""Workload 2's step (MiniGPT layer set, delayed scaling, forward and backward) captured as one
+HIP graph: every replay must give exactly what the same step gives launched call by call.
+
+The step is the one bench.py times.  Its entry points allocate nothing and record no memset,
+so the whole step (9 cast-transposes, 9 GEMMs, the recipe update) goes into the graph.  The
+replays run with eager device work and host synchronisation between them, and each replay's
+recipe state (history, scales), codes and GEMM outputs are compared bit for bit with the
+matching eager step from the same starting state."""
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import DEV, announce  # noqa: E402
+
+
+def _snapshot(step):
+    return [t.detach().clone() for t in step.outputs()]
+
+
+def test_minigpt_step_graph_replays_match_eager():
+    import bench
+    import scaled_quantize_gemm_amd as sq
+    import workloads
+
+    announce("graph: MiniGPT step, eager reference")
+    step = bench.MiniGPTStep(sq, workloads, torch.device(DEV))
+    st = step.state
+    start = [st.amax_history.clone(), st.scale.clone(), st.scale_inv.clone()]
+    n = 3
+    eager = []
+    for _ in range(n):
+        step()
+        torch.cuda.synchronize()
+        eager.append(_snapshot(step))
+    # the recipe state moved on every step, so the steps differ from one another
+    assert not torch.equal(eager[0][1], eager[-1][1]) or not torch.equal(eager[0][0], eager[-1][0])
+
+    announce("graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    # capture launches nothing: back to the starting state, in place (the graph holds addresses)
+    for dst, src in zip((st.amax_history, st.scale, st.scale_inv), start):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for k in range(n):
+        announce("graph: replay", k)
+        g.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(step)
+        for i, (a, b) in enumerate(zip(got, eager[k])):
+            assert a.dtype == b.dtype and a.shape == b.shape
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}: output {i} differs"
+        # eager work of the program's own between replays
+        torch.ones(1 << 20, device=DEV).mul_(2.0).sum().item()
