@@ -174,7 +174,7 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
   const int r16 = t >> 4, cg = t & 15;
   const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
   // the tile stays as loaded (packed bf16: 16 VGPRs) until the cast widens it: widened at the
-  // load, the kernel held 70 VGPRs (3 blocks per CU)
+  // load, the 1x128 mode held 110 VGPRs (2 blocks per CU) and the others ~70 (3); now 56-60 (4)
   Raw8<BF16> raw[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) raw[p] = load_raw8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols);
@@ -321,7 +321,7 @@ static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* sca
   const int64_t blocks = ntiles < 0x7FFFFFFF ? ntiles : 0x7FFFFFFF;
   if (rows % 128 == 0 && cols % 128 == 0 && (rows >> 7) * (cols >> 7) < 0x7FFFFFFF) {
     // 128 x 128 tiles, the blockwise kernel with the per-tensor scale: whole 128-byte lines of q
-    // and qT (8192 x 14336 bf16: 92 us against 132 us on 64 x 64 tiles, inputs and outputs
+    // and qT (8192 x 14336 bf16: 88-91 us against 132 us on 64 x 64 tiles, inputs and outputs
     // beyond the last-level cache)
     // 20 KB of unused dynamic LDS hold residency at 3 blocks per CU (41 KB each of 160 KB): at
     // the 4 its registers allow, this launch measured 2-5% slower at workload 4's shapes
