@@ -16,9 +16,16 @@ Printed: one JSON line.  value = the step's GEMM FLOPs / step time (TFLOP/s, the
 step, casts included); the GEMM's duration from HIP events on the launch stream around it
 in the timed steps, the other calls' from a second pass of the same steps; roofline of the
 dominant kernel (the GEMM, against dense FP8 MFMA peak) and of the standalone amax + cast
-stream (against HBM peak, timed over back-to-back launches after the steps); the CPU
-oracle timed on a bounded sample.  `--next-rows` times the LayerNorm + cast and the fused
-GEMM epilogues on workload 4's shapes instead.
+stream (against HBM peak, timed over back-to-back launches after the steps) and of the
+per-tensor cast-transpose of workload 4's gradient (against HBM peak, with a device copy of
+the same read:write mix beside it); the CPU oracle timed on a bounded sample.
+
+Other lines, each printed instead of the main one:
+  --blockwise   workload 3 (1x128 x 128x128 current scaling): quantizers, blockwise
+                cast-transposes, forward / dgrad / wgrad GEMMs
+  --minigpt     workload 2 (MiniGPT layer set, delayed scaling): the whole step, eager and
+                as one captured graph
+  --next-rows   workload 4's LayerNorm + cast and fused GEMM epilogues, and its backward GEMMs
 """
 
 from __future__ import annotations
