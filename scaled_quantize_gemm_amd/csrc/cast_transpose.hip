@@ -139,7 +139,12 @@ constexpr int kBwPitch = 33;
 // cast-transpose of 128-aligned shapes, whose 128-byte row pieces of q and qT are whole cache
 // lines where the 64 x 64 kernel writes half lines)
 constexpr int kBwTile = 1, kBwBlock = 2, kBwTensor = 0;
+// the kernel's static LDS (qT code tile, column-amax partials, column scales) and the dynamic
+// padding that holds the per-tensor launch at 3 resident blocks of the CU's 160 KB
+constexpr size_t kBwStaticLds = 128 * kBwPitch * 4 + 8 * 128 * 4 + 128 * 4;
 constexpr size_t kCtTensorLdsPad = 20 * 1024;
+static_assert(3 * (kBwStaticLds + kCtTensorLdsPad) <= 160 * 1024 && 4 * (kBwStaticLds + kCtTensorLdsPad) > 160 * 1024,
+              "the LDS padding must leave room for exactly 3 blocks per CU");
 
 template <int FMT, bool BF16, int KIND>
 __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __restrict__ x, int64_t rows,
