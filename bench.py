@@ -21,6 +21,7 @@ per-tensor cast-transpose of workload 4's gradient (against HBM peak, with a dev
 the same read:write mix beside it); the CPU oracle timed on a bounded sample.
 
 Other lines, each printed instead of the main one:
+  --workload1   workload 1 (256x256 per-tensor delayed scaling, fp32): the 16-step loop
   --blockwise   workload 3 (1x128 x 128x128 current scaling): quantizers, blockwise
                 cast-transposes, forward / dgrad / wgrad GEMMs
   --minigpt     workload 2 (MiniGPT layer set, delayed scaling): the whole step, eager and
@@ -247,6 +248,39 @@ class MiniGPTStep:
         return out
 
 
+def workload1_rows(sq, workloads, dev, steps, warmup):
+    """Workload 1, the correctness configuration: X [256x256] fp32 ~N(0,1) drawn fresh for each
+    of 16 steps, W [256x256] ~N(0,0.02); per-tensor delayed scaling (history 16, max, margin 0),
+    E4M3 both, Y = X W^T in fp32; a step is cast X, cast W, GEMM, recipe update (4 launches,
+    33.6 MFLOP).  Timed over the 16 steps repeated (the inputs already on the device)."""
+    import torch
+
+    W = workloads.w1_weight().to(dev)
+    Xs = [workloads.w1_input(t).to(dev) for t in range(16)]
+    st = sq.DelayedScalingState([sq.FP8_E4M3, sq.FP8_E4M3], history_len=16, device=str(dev))
+    (sx, ax, ix), (sw, aw, iw) = st.slot(0), st.slot(1)
+    qx = torch.empty((256, 256), dtype=torch.uint8, device=dev)
+    qw = torch.empty_like(qx)
+    Y = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    turn = [0]
+
+    def step():
+        t = turn[0] = (turn[0] + 1) % 16
+        sq.fp8_quantize(Xs[t], sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sx, amax_slot=ax, q=qx)
+        sq.fp8_quantize(W, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sw, amax_slot=aw, q=qw)
+        sq.fp8_gemm(qx, sq.FP8_E4M3, ix, 0, qw, sq.FP8_E4M3, iw, 0, sq.OUT_F32, C=Y)
+        st.update()
+
+    us = _time_us(step, steps, warmup)
+    flops = 2.0 * 256 ** 3
+    return {"metric": "workload 1 step (256x256 per-tensor delayed scaling): us per step", "steps": steps,
+            "warmup": warmup,
+            "config": {"workload": "workload 1: X [256x256] fp32 ~N(0,1) fresh per step, W ~N(0,0.02); E4M3, "
+                                   "history 16, max, margin 0; fp32 out", "launches_per_step": 4},
+            "us_per_step": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 2),
+            "bound": "launch latency (4 launches of a few microseconds each)"}
+
+
 def minigpt_rows(sq, workloads, dev, steps, warmup):
     """Workload 2's step, launched call by call and as one captured graph (19 launches of
     kernels a few microseconds long: launch-bound)."""
@@ -372,6 +406,8 @@ def main():
     ap.add_argument("--next-rows", action="store_true",
                     help="time the fusions around the path instead (LayerNorm + cast, fused GEMM epilogue) "
                          "on workload 4's shapes; prints their own JSON line")
+    ap.add_argument("--workload1", action="store_true",
+                    help="time workload 1's step (256x256 per-tensor delayed scaling, fp32); prints its own JSON line")
     ap.add_argument("--minigpt", action="store_true",
                     help="time workload 2's step (MiniGPT layer set, delayed scaling, forward and backward) "
                          "eager and as a captured graph; prints its own JSON line")
@@ -402,6 +438,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
+        return
+
+    if args.workload1:
+        print(json.dumps(workload1_rows(sq, workloads, dev, args.steps, args.warmup)))
         return
 
     if args.minigpt:
