@@ -646,6 +646,11 @@ constexpr int BLK_NST = 3;
 // the tile row held at LDS row q of a 64-row slab layout (tile i's MFMA row t at 16i + t is
 // slab row 4t + i)
 __device__ __forceinline__ int blk_row_of(int q) { return (q & ~63) + 4 * (q & 15) + ((q >> 4) & 3); }
+// the B row (output column) held at LDS row q of a slab of 16 NT columns: MFMA tile j's
+// column t at LDS row 16j + t is slab column NT t + j (NT = 4: the same map as the rows)
+__device__ __forceinline__ int blk_col_of(int q, int nt) {
+  return (q & ~(16 * nt - 1)) + nt * (q & 15) + ((q >> 4) & (nt - 1));
+}
 // position of 16-byte chunk c in 128-byte LDS row q (the small-tile kernel's swizzle)
 __device__ __forceinline__ int blk_pos(int q, int c) { return c ^ (((q >> 1) ^ ((q & 1) << 2)) & 7); }
 
@@ -653,15 +658,29 @@ __device__ __forceinline__ int blk_pos(int q, int c) { return c ^ (((q >> 1) ^ (
 // per 1x128 run along K: one per column per stage, [K/128][N]) or MODE_TENSOR (no scale loads;
 // the MFMAs accumulate straight into acc and the epilogue multiplies by sa * sb: the 256 x 128
 // tile gives small per-tensor problems twice the tiles of the 256 x 256 kernel)
-template <int MODE, int FA, int FB, int OUT, bool FUSED>
+// the tile-width-dependent shape of the kernel below: NT MFMA column tiles per wave slab of SW
+// columns; the B rows of a stage are BN x 128 B, loaded as NB of the stage's NOPS 1 KB
+// operations (OPW per wave).
+template <int BN>
+struct BlkShape {
+  static constexpr int NT = BN / 32, SW = BN / 2, NB = BN / 8, NOPS = 32 + NB, OPW = NOPS / 8;
+  static constexpr int SA_OFF = BLK_B_OFF + BN * BLK_BK, SB_OFF = SA_OFF + 1024, STAGE = SB_OFF + 1024;
+};
+
+template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN>
 __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                           const float* __restrict__ sa_p,
                                                           const float* __restrict__ sb_p, const EpiParams ep, int M,
                                                           int N, int K, int tiles_m, int tiles_n) {
-  constexpr int STAGE = BLK_STAGE, NST = BLK_NST, D = NST - 1, U = NST;
   constexpr bool TENSOR = MODE == MODE_TENSOR;
+  static_assert(BN == BLK_BN || (BN == 64 && TENSOR), "256 x 64 tiles serve per-tensor scaling only");
+  using Shape = BlkShape<BN>;
+  constexpr int NT = Shape::NT, SW = Shape::SW, NOPS = Shape::NOPS, OPW = Shape::OPW;
+  constexpr int SA_OFF = Shape::SA_OFF, SB_OFF = Shape::SB_OFF, STAGE = Shape::STAGE;
+  constexpr int NST = BLK_NST, D = NST - 1, U = NST;
+  static_assert(NOPS % 8 == 0, "every wave issues the same number of loads");
   static_assert(NST * STAGE <= 160 * 1024, "LDS ring must fit the 160 KB of a CU");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[BLK_NST * Shape::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -669,10 +688,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   const int g = lane >> 4, r = lane & 15;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BLK_BM, n0 = tn * BLK_BN;
+  const int m0 = tm * BLK_BM, n0 = tn * BN;
   const int nk = K / BLK_BK;
 
-  // ---- loads: 48 x 1 KB of tile data per stage, 6 per wave (ops 0..31 are A, 32..47 B), and
+  // ---- loads: NOPS x 1 KB of tile data per stage, OPW per wave (ops 0..31 are A, then B), and
   //      one scale load per wave (waves 0-3: 64 row scales each; 4-7: a copy of the block scale)
   const int lim_a = M - m0, lim_b = N - n0;
   const uint64_t a_bytes = (uint64_t)lim_a * K, b_bytes = (uint64_t)lim_b * K;
@@ -682,12 +701,15 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(B + (size_t)n0 * K), (short)0, (int)(b_bytes < 0xFFFFFFFFull ? b_bytes : 0xFFFFFFFFull),
       kBufferFlags);
+  // fixed size, OPW <= 6 of them used: sized by OPW, the array made the host compiler drop
+  // this kernel's launch stubs (every instantiation, with no diagnostic)
+  static_assert(OPW <= 6, "load offsets per wave");
   uint32_t od[6];
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int o = wave * 6 + i, local = o < 32 ? o : o - 32;
+  for (int i = 0; i < OPW; ++i) {
+    const int o = wave * OPW + i, local = o < 32 ? o : o - 32;
     const int slot = local * 64 + lane, q = slot >> 3, c = blk_pos(q, slot & 7);
-    const int row = blk_row_of(q), lim = o < 32 ? lim_a : lim_b;
+    const int row = o < 32 ? blk_row_of(q) : blk_col_of(q, NT), lim = o < 32 ? lim_a : lim_b;
     od[i] = (uint32_t)(row < lim ? row : lim - 1) * (uint32_t)K + c * 16;
   }
   const int nkb = nk;
@@ -714,27 +736,27 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     const int col = (wave & 1) * 64 + lane;
     s_voff = (uint32_t)(col < lim_b ? col : lim_b - 1) * 4;
   }
-  const int s_lds = s_is_a ? BLK_SA_OFF + wave * 256 : BLK_SB_OFF + (wave - 4) * 256;
+  const int s_lds = s_is_a ? SA_OFF + wave * 256 : SB_OFF + (wave - 4) * 256;
   const uint32_t s_step = s_is_a ? (uint32_t)M * 4 : (MODE == MODE_BLOCK ? 4u : (uint32_t)N * 4);
   auto issue = [&](int ks, int st) {
     uint8_t* buf = smem + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < 6; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave * 6 + i < 32 ? ra : rb, (lds_ptr_t)(buf + (wave * 6 + i) * 1024), 16,
-                                               od[i], ks * BLK_BK, 0, 0);
+    for (int i = 0; i < OPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave * OPW + i < 32 ? ra : rb, (lds_ptr_t)(buf + (wave * OPW + i) * 1024),
+                                               16, od[i], ks * BLK_BK, 0, 0);
     if constexpr (!TENSOR)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(buf + s_lds), 4, s_voff, ks * s_step, 0, 0);
   };
-  // wait until at most `later` stages of this wave's loads (7 per stage, 6 per tensor) are in
-  // flight
+  // wait until at most `later` stages of this wave's loads (OPW per stage, + 1 scale load
+  // unless per tensor) are in flight
   auto wait_stage = [&](int later) {
-    if (later >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(TENSOR ? 6 : 7) : "memory");
+    if (later >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(TENSOR ? OPW : OPW + 1) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
   // ---- per-lane LDS bases per stage (immediates add the tile offsets)
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const int slab_a = grp * 128 + wr * 64, slab_b = wc * 64;
+  const int slab_a = grp * 128 + wr * 64, slab_b = wc * SW;
   uint32_t a_lo[NST], a_hi[NST], b_lo[NST], b_hi[NST], s_a[NST], s_b[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
@@ -744,16 +766,16 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     a_hi[st] = base + qa * 128 + (blk_pos(qa, g + 4) << 4);
     b_lo[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g) << 4);
     b_hi[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g + 4) << 4);
-    s_a[st] = base + BLK_SA_OFF + (slab_a + 16 * g) * 4;
-    s_b[st] = base + BLK_SB_OFF + (MODE == MODE_TILE2 ? (slab_b + 4 * r) * 4 : 0);
+    s_a[st] = base + SA_OFF + (slab_a + 16 * g) * 4;
+    s_b[st] = base + SB_OFF + (MODE == MODE_TILE2 ? (slab_b + 4 * r) * 4 : 0);
   }
 
-  v4f acc[4][4];
+  v4f acc[4][Shape::NT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  v8i fa[4], fb[4];
+    for (int j = 0; j < NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i fa[4], fb[Shape::NT];
   float fsa[16], fsb[4] = {0.f, 0.f, 0.f, 0.f};
   auto pack = [](const u32x4& lo, const u32x4& hi) -> v8i {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -768,8 +790,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     fa[3] = pack(ds_read16<3 * 2048>(a_lo[ST]), ds_read16<3 * 2048>(a_hi[ST]));
     fb[0] = pack(ds_read16<0 * 2048>(b_lo[ST]), ds_read16<0 * 2048>(b_hi[ST]));
     fb[1] = pack(ds_read16<1 * 2048>(b_lo[ST]), ds_read16<1 * 2048>(b_hi[ST]));
-    fb[2] = pack(ds_read16<2 * 2048>(b_lo[ST]), ds_read16<2 * 2048>(b_hi[ST]));
-    fb[3] = pack(ds_read16<3 * 2048>(b_lo[ST]), ds_read16<3 * 2048>(b_hi[ST]));
+    if constexpr (NT == 4) {
+      fb[NT > 2 ? 2 : 0] = pack(ds_read16<2 * 2048>(b_lo[ST]), ds_read16<2 * 2048>(b_hi[ST]));
+      fb[NT > 3 ? 3 : 0] = pack(ds_read16<3 * 2048>(b_lo[ST]), ds_read16<3 * 2048>(b_hi[ST]));
+    }
     if constexpr (TENSOR) return;
     const u32x4 s0 = ds_read16<0>(s_a[ST]), s1 = ds_read16<16>(s_a[ST]), s2 = ds_read16<32>(s_a[ST]),
                 s3 = ds_read16<48>(s_a[ST]);
@@ -796,13 +820,13 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   auto compute = [&]() {
     if constexpr (TENSOR) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t >> 2], fb[t & 3], acc[t >> 2][t & 3],
-                                                                               FA, FB, 0, 0, 0, 0);
+      for (int t = 0; t < 4 * NT; ++t) {
+        acc[t / NT][t % NT] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t / NT], fb[t % NT],
+                                                                                acc[t / NT][t % NT], FA, FB, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       return;
-    }
+    } else {
     float sab[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sab[e] = MODE == MODE_BLOCK ? fsa[e] * fsb[0] : fsa[e];
@@ -823,6 +847,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     }
     fold(14);
     fold(15);
+    }
   };
   auto barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -871,14 +896,14 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       }, std::make_integer_sequence<int, U>{});
   }
 
-  // ---- epilogue: acc[i][j][jj] is tile row slab + 16g + 4jj + i, column slab + 4r + j
+  // ---- epilogue: acc[i][j][jj] is tile row slab + 16g + 4jj + i, column slab + NT r + j
   Epilogue<OUT, FUSED> epi(ep);
   float scale = 1.0f;
   if constexpr (TENSOR) scale = sa_p[0] * sb_p[0];
-  const int gn = n0 + slab_b + 4 * r;
-  const bool quad = (N & 3) == 0 && gn + 3 < N;  // all four columns present, store aligned
-  float b[4];
-  epi.template bias<4>(gn, N, b);
+  const int gn = n0 + slab_b + NT * r;
+  const bool quad = N % NT == 0 && gn + NT - 1 < N;  // all NT columns present, store aligned
+  float b[Shape::NT];
+  epi.template bias<Shape::NT>(gn, N, b);
   epi.with_act([&](auto act_c) {
     constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
@@ -887,10 +912,12 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       for (int i = 0; i < 4; ++i) {
         const int gm = m0 + slab_a + 16 * g + 4 * jj + i;
         if (gm >= M) continue;
-        float v[4] = {acc[i][0][jj], acc[i][1][jj], acc[i][2][jj], acc[i][3][jj]};
+        float v[Shape::NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) v[c] = acc[i][c][jj];
         if constexpr (TENSOR) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] *= scale;
+          for (int c = 0; c < NT; ++c) v[c] *= scale;
         }
         epi.pre(v, b);
         epi.aux(v, gm, gn, N, quad);
@@ -899,6 +926,9 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   });
   epi.finish(lane, reinterpret_cast<uint32_t*>(smem));
 }
+
+// per-tensor problems with fewer 256 x 128 tiles than this run on 256 x 64 tiles
+constexpr int64_t kNarrowTiles = 128;
 
 template <int MODE, int FA, int FB, int OUT, bool FUSED>
 static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, const EpiParams& ep, int M,
@@ -910,7 +940,15 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
     const int64_t big_tiles = (int64_t)((M + BIG_BM - 1) / BIG_BM) * ((N + BIG_BN - 1) / BIG_BN);
     if (big_tiles < 256 && 256ll * K < (1ll << 32)) {
       const int tiles_m = (M + BLK_BM - 1) / BLK_BM, tiles_n = (N + BLK_BN - 1) / BLK_BN;
-      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+      if ((int64_t)tiles_m * tiles_n < kNarrowTiles) {
+        // still a fraction of the CUs: 256 x 64 tiles double the count
+        const int tiles_n64 = (N + 63) / 64;
+        hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, 64>), dim3(tiles_m * tiles_n64), dim3(512), 0, st,
+                           A, B, static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m,
+                           tiles_n64);
+        return check_launch(what);
+      }
+      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, BLK_BN>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
                          static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m, tiles_n);
       return check_launch(what);
     }
@@ -940,7 +978,7 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
     const int64_t mn = M > N ? M : N;
     const bool offsets32 = 256ll * K < (1ll << 32) && (int64_t)(K / 128) * mn * 4 < (1ll << 32);
     if (offsets32) {
-      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, BLK_BN>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
                          static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m, tiles_n);
       return check_launch(what);
     }
