@@ -416,8 +416,9 @@ def main():
                          "cast-transposes, forward / dgrad / wgrad GEMMs); prints their own JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus N with N > 1 is not supported "
-              "(the quantizers shard rows without communication; see the sharding notes)", file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus N with N > 1 is not supported (the library has no "
+              "multi-GPU path: its quantizers would shard rows without communication, per-tensor amaxes would "
+              "need one all-reduce MAX per step)", file=sys.stderr)
         sys.exit(2)
 
     import torch
