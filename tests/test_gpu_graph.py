@@ -19,13 +19,16 @@ def _snapshot(step):
     return [t.detach().clone() for t in step.outputs()]
 
 
-def test_minigpt_step_graph_replays_match_eager():
+@pytest.mark.parametrize("streams", [1, 3])
+def test_minigpt_step_graph_replays_match_eager(streams):
+    """streams=3: each layer's casts and GEMMs forked over three streams and joined by events,
+    so the graph holds a DAG; its replays must still equal the eager steps bit for bit."""
     import bench
     import scaled_quantize_gemm_amd as sq
     import workloads
 
-    announce("graph: MiniGPT step, eager reference")
-    step = bench.MiniGPTStep(sq, workloads, torch.device(DEV))
+    announce("graph: MiniGPT step, eager reference, streams", streams)
+    step = bench.MiniGPTStep(sq, workloads, torch.device(DEV), streams=streams)
     st = step.state
     start = [st.amax_history.clone(), st.scale.clone(), st.scale_inv.clone()]
     n = 3
@@ -37,7 +40,7 @@ def test_minigpt_step_graph_replays_match_eager():
     # the recipe state moved on every step, so the steps differ from one another
     assert not torch.equal(eager[0][1], eager[-1][1]) or not torch.equal(eager[0][0], eager[-1][0])
 
-    announce("graph: capture")
+    announce("graph: capture, streams", streams)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
@@ -47,7 +50,7 @@ def test_minigpt_step_graph_replays_match_eager():
         dst.copy_(src)
     torch.cuda.synchronize()
     for k in range(n):
-        announce("graph: replay", k)
+        announce("graph: replay", k, "streams", streams)
         g.replay()
         torch.cuda.synchronize()
         got = _snapshot(step)
