@@ -290,37 +290,66 @@ class MiniGPTStep:
         return out
 
 
+class Workload1Step:
+    """One step of workload 1 (the correctness configuration): X [256x256] fp32 ~N(0,1) drawn
+    fresh for each of 16 steps (the step index advances on the host), W [256x256] ~N(0,0.02);
+    per-tensor delayed scaling (history 16, max, margin 0), E4M3 both, Y = X W^T in fp32: cast X,
+    cast W, GEMM, recipe update.  Buffers are allocated up front (graph capture)."""
+
+    def __init__(self, sq, workloads, dev):
+        import torch
+
+        self.sq = sq
+        self.W = workloads.w1_weight().to(dev)
+        self.Xs = [workloads.w1_input(t).to(dev) for t in range(16)]
+        self.state = sq.DelayedScalingState([sq.FP8_E4M3, sq.FP8_E4M3], history_len=16, device=str(dev))
+        self.qx = torch.empty((256, 256), dtype=torch.uint8, device=dev)
+        self.qw = torch.empty_like(self.qx)
+        self.Y = torch.empty((256, 256), dtype=torch.float32, device=dev)
+        self.t = 0
+
+    def __call__(self):
+        sq = self.sq
+        (sx, ax, ix), (sw, aw, iw) = self.state.slot(0), self.state.slot(1)
+        X = self.Xs[self.t]
+        self.t = (self.t + 1) % 16
+        sq.fp8_quantize(X, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sx, amax_slot=ax, q=self.qx)
+        sq.fp8_quantize(self.W, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sw, amax_slot=aw, q=self.qw)
+        sq.fp8_gemm(self.qx, sq.FP8_E4M3, ix, 0, self.qw, sq.FP8_E4M3, iw, 0, sq.OUT_F32, C=self.Y)
+        self.state.update()
+
+    def outputs(self):
+        return [self.state.amax_history, self.state.scale, self.state.scale_inv, self.qx, self.qw, self.Y]
+
+
 def workload1_rows(sq, workloads, dev, steps, warmup):
-    """Workload 1, the correctness configuration: X [256x256] fp32 ~N(0,1) drawn fresh for each
-    of 16 steps, W [256x256] ~N(0,0.02); per-tensor delayed scaling (history 16, max, margin 0),
-    E4M3 both, Y = X W^T in fp32; a step is cast X, cast W, GEMM, recipe update (4 launches,
-    33.6 MFLOP).  Timed over the 16 steps repeated (the inputs already on the device)."""
+    """Workload 1's loop (cast X, cast W, GEMM, update at 256x256; 4 launches, 33.6 MFLOP per
+    step), launched call by call and with the 16-step loop captured as one graph."""
     import torch
 
-    W = workloads.w1_weight().to(dev)
-    Xs = [workloads.w1_input(t).to(dev) for t in range(16)]
-    st = sq.DelayedScalingState([sq.FP8_E4M3, sq.FP8_E4M3], history_len=16, device=str(dev))
-    (sx, ax, ix), (sw, aw, iw) = st.slot(0), st.slot(1)
-    qx = torch.empty((256, 256), dtype=torch.uint8, device=dev)
-    qw = torch.empty_like(qx)
-    Y = torch.empty((256, 256), dtype=torch.float32, device=dev)
-    turn = [0]
-
-    def step():
-        t = turn[0] = (turn[0] + 1) % 16
-        sq.fp8_quantize(Xs[t], sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sx, amax_slot=ax, q=qx)
-        sq.fp8_quantize(W, sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=sw, amax_slot=aw, q=qw)
-        sq.fp8_gemm(qx, sq.FP8_E4M3, ix, 0, qw, sq.FP8_E4M3, iw, 0, sq.OUT_F32, C=Y)
-        st.update()
-
+    step = Workload1Step(sq, workloads, dev)
     us = _time_us(step, steps, warmup)
+    # the 16-step loop captured as one graph (64 launches; each step's X is fixed at capture)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(16):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        for _ in range(16):
+            step()
+    graph_us = _time_us(g.replay, max(1, steps // 16), max(1, warmup // 16)) / 16
     flops = 2.0 * 256 ** 3
     return {"metric": "workload 1 step (256x256 per-tensor delayed scaling): us per step", "steps": steps,
             "warmup": warmup,
             "config": {"workload": "workload 1: X [256x256] fp32 ~N(0,1) fresh per step, W ~N(0,0.02); E4M3, "
                                    "history 16, max, margin 0; fp32 out", "launches_per_step": 4},
             "us_per_step": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 2),
-            "bound": "launch latency (4 launches of a few microseconds each)"}
+            "graph_us_per_step": round(graph_us, 2),
+            "bound": "launch latency (4 launches of a few microseconds each); the graph is the 16-step loop "
+                     "captured once"}
 
 
 def minigpt_rows(sq, workloads, dev, steps, warmup):

@@ -1,8 +1,10 @@
-"""Workload 2's step (MiniGPT layer set, delayed scaling, forward and backward) captured as one
-HIP graph: every replay must give exactly what the same step gives launched call by call.
+"""Steps captured as HIP graphs: every replay must give exactly what the same steps give
+launched call by call.  Workload 2's step (MiniGPT layer set, delayed scaling, forward and
+backward: 9 cast-transposes, 9 GEMMs, the recipe update) on one stream and forked over three,
+and workload 1's 16-step loop (per-tensor quantize of X and W, GEMM, update).
 
-The step is the one bench.py times.  Its entry points allocate nothing and record no memset,
-so the whole step (9 cast-transposes, 9 GEMMs, the recipe update) goes into the graph.  The
+The steps are the ones bench.py times.  Their entry points allocate nothing and record no
+memset, so every call goes into the graph.  The
 replays run with eager device work and host synchronisation between them, and each replay's
 recipe state (history, scales), codes and GEMM outputs are compared bit for bit with the
 matching eager step from the same starting state."""
@@ -58,4 +60,40 @@ def test_minigpt_step_graph_replays_match_eager(streams):
             assert a.dtype == b.dtype and a.shape == b.shape
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}: output {i} differs"
         # eager work of the program's own between replays
+        torch.ones(1 << 20, device=DEV).mul_(2.0).sum().item()
+
+
+def test_workload1_loop_graph_replays_match_eager():
+    """Workload 1's 16 steps (per-tensor fp8_quantize of X and W, GEMM, recipe update) captured
+    as one graph: two replays from the starting state equal eager steps 1-16 and 17-32."""
+    import bench
+    import scaled_quantize_gemm_amd as sq
+    import workloads
+
+    announce("graph: workload 1 loop, eager reference")
+    step = bench.Workload1Step(sq, workloads, torch.device(DEV))
+    st = step.state
+    start = [st.amax_history.clone(), st.scale.clone(), st.scale_inv.clone()]
+    eager = []
+    for _ in range(2):
+        for _ in range(16):
+            step()
+        torch.cuda.synchronize()
+        eager.append(_snapshot(step))
+    assert step.t == 0
+    announce("graph: workload 1 capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(16):
+            step()
+    torch.cuda.synchronize()
+    for dst, src in zip((st.amax_history, st.scale, st.scale_inv), start):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for k in range(2):
+        announce("graph: workload 1 replay", k)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(_snapshot(step), eager[k])):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}: output {i} differs"
         torch.ones(1 << 20, device=DEV).mul_(2.0).sum().item()
