@@ -94,26 +94,34 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // compares above +inf, so an unsigned max propagates NaN.
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
-// Unsigned max over the 64 lanes of a wave (result in every lane).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-    v = v > o ? v : o;
-  }
+// Lane exchanges on the DPP path (a VALU operand modifier, no LDS round trip): each lane reads
+// its partner's value under a quad swap (lane ^ 1, lane ^ 2), a reversal of its 8-lane half-row
+// or a reversal of its 16-lane row.  Every step of the reductions below combines a lane with a
+// partner that in turn reads it, so all lanes of a group end with the same result.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Unsigned max over aligned groups of W lanes (W = 2, 4, 8, 16, 32, 64; result in every lane):
+// DPP within a row of 16, lane shuffles across rows.
+template <int W>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group of 2^k lanes");
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_partner<kDppQuadXor1>(v));
+  if constexpr (W >= 4) v = mx(v, dpp_partner<kDppQuadXor2>(v));
+  if constexpr (W >= 8) v = mx(v, dpp_partner<kDppHalfMirror>(v));
+  if constexpr (W >= 16) v = mx(v, dpp_partner<kDppMirror>(v));
+  if constexpr (W >= 32) v = mx(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  if constexpr (W >= 64) v = mx(v, (uint32_t)__shfl_xor((int)v, 32, 64));
   return v;
 }
 
-// Unsigned max over aligned groups of W lanes (W = 2, 4, 8, 16, 32).
-template <int W>
-__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = W / 2; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-    v = v > o ? v : o;
-  }
-  return v;
-}
+// Unsigned max over the 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return group_max_u32<64>(v); }
 
 // Current-scaling rule: s = fmax / amax (correctly rounded), overflow clamped to FLT_MAX;
 // amax zero or not finite -> s = 1.  s_inv = 1 / s.

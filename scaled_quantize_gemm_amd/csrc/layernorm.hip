@@ -23,9 +23,18 @@ namespace sfp8 {
 
 constexpr int kLnRows = 4;  // waves per block, one row each per step (small blocks pack the CU)
 
+// sum over the 64 lanes, the same in every lane (each step adds a lane and its partner, which
+// adds them in the other order: fp32 addition commutes); 6 levels, as the error bound assumes
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  auto partner = [](float x, auto ctrl) {
+    return __uint_as_float(dpp_partner<decltype(ctrl)::value>(__float_as_uint(x)));
+  };
+  v += partner(v, std::integral_constant<int, kDppQuadXor1>{});
+  v += partner(v, std::integral_constant<int, kDppQuadXor2>{});
+  v += partner(v, std::integral_constant<int, kDppHalfMirror>{});
+  v += partner(v, std::integral_constant<int, kDppMirror>{});
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
   return v;
 }
 
