@@ -112,6 +112,30 @@ def test_tensor_scaled_gemm(sq, fa, fb, out, mnk):
         check_gemm(np_of(C), Cr, S, G, K, "tensor", out == 1, f"tensor {mnk} {fa}{fb} out{out} real={realistic}")
 
 
+# per-tensor problems below 128 tiles of 256 x 128 run on 256 x 64 tiles, from 128 tiles on on
+# 256 x 128 tiles (and from 256 tiles of 256 x 256 on the 256 x 256 kernel): both sides of each
+# boundary, with ragged last tiles, against the oracle on sampled rows
+@pytest.mark.parametrize("mnk", [
+    (256, 127 * 128, 256),       # 127 tiles of 256 x 128: 256 x 64 tiles
+    (256, 128 * 128, 256),       # 128: 256 x 128 tiles
+    (2 * 256 - 5, 8024, 384),    # 2 x 63 = 126, ragged M and N: 256 x 64 tiles
+    (2 * 256, 64 * 128, 128),    # 2 x 64 = 128: 256 x 128 tiles
+    (3840, 4096, 128),           # 15 x 16 = 240 tiles of 256 x 256: 256 x 128 tiles
+    (4096, 4096 - 3, 128),       # 256 tiles of 256 x 256, ragged N: the 256 x 256 kernel
+])
+def test_tensor_gemm_tile_width_boundaries(sq, mnk):
+    M, N, K = mnk
+    announce("tensor gemm tile-width boundary", mnk)
+    rng = np.random.default_rng(M + 5 * N + K)
+    A, B = _codes(rng, (M, K), 0), _codes(rng, (N, K), 1)
+    sa, sb = np.float32(0.03), np.float32(0.002)
+    C = sq.fp8_gemm(_t(A), 0, _scal(sa), 0, _t(B), 1, _scal(sb), 0, sq.OUT_BF16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([rng.choice(M, min(M, 24), replace=False), [0, M - 1]]))
+    Cr, S, G = og.gemm_ref(A, 0, sa, og.TENSOR, B, 1, sb, og.TENSOR, rows=rows)
+    check_gemm(np_of(C)[rows], Cr, S, G, K, "tensor", True, f"tile-width boundary {mnk}")
+
+
 @pytest.mark.parametrize("out", [0, 1])
 @pytest.mark.parametrize("mnk", [(256, 256, 256), (200, 300, 512), (1, 130, 128), (129, 257, 384)])
 def test_blockwise_gemm(sq, out, mnk):
