@@ -927,7 +927,8 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   epi.finish(lane, reinterpret_cast<uint32_t*>(smem));
 }
 
-// per-tensor problems with fewer 256 x 128 tiles than this run on 256 x 64 tiles
+// per-tensor problems with fewer 256 x 128 tiles than this run on 256 x 64 tiles (at 200, the
+// 144- and 192-tile GEMMs of the MiniGPT layer set moved too and its step got 5-7% slower)
 constexpr int64_t kNarrowTiles = 128;
 
 template <int MODE, int FA, int FB, int OUT, bool FUSED>
