@@ -23,7 +23,7 @@ the same read:write mix beside it); the CPU oracle timed on a bounded sample.
 Other lines, each printed instead of the main one:
   --workload1   workload 1 (256x256 per-tensor delayed scaling, fp32): the 16-step loop
   --blockwise   workload 3 (1x128 x 128x128 current scaling): quantizers, blockwise
-                cast-transposes, forward / dgrad / wgrad GEMMs
+                cast-transposes, forward / dgrad / wgrad GEMMs, and the whole training step
   --minigpt     workload 2 (MiniGPT layer set, delayed scaling): the whole step on one and on
                 three streams, eager and as one captured graph
   --next-rows   workload 4's LayerNorm + cast and fused GEMM epilogues, and its backward GEMMs
@@ -358,22 +358,10 @@ def minigpt_rows(sq, workloads, dev, steps, warmup):
     line's figure is the fastest of the four, all four are listed."""
     import torch
 
-    def timed(step):
-        eager_us = _time_us(step, steps, warmup)
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        with torch.cuda.graph(g):
-            step()
-        return eager_us, _time_us(g.replay, steps, warmup)
-
     one = MiniGPTStep(sq, workloads, dev)
-    eager1, graph1 = timed(one)
+    eager1, graph1 = _step_timings(one, steps, warmup)
     three = MiniGPTStep(sq, workloads, dev, streams=3)
-    eager3, graph3 = timed(three)
+    eager3, graph3 = _step_timings(three, steps, warmup)
     runs = {"one stream, eager": eager1, "one stream, graph": graph1, "three streams, eager": eager3,
             "three streams, graph": graph3}
     best = min(runs, key=runs.get)
@@ -390,6 +378,107 @@ def minigpt_rows(sq, workloads, dev, steps, warmup):
             "schedules": "three streams: each layer's casts, then its GEMMs, forked over three streams and "
                          "joined by events (eager launches are host-bound on the stream switches; the graph "
                          "replays the DAG)"}
+
+
+class BlockwiseStep:
+    """One training step of workload 3's layer under blockwise current scaling (E4M3, bf16 out):
+    the blockwise cast-transposes of X (1x128 runs), W (128x128 blocks) and dY (1x128 runs),
+    whose q / qT outputs feed the forward Y = X W^T (TILE x BLOCK), dgrad dX = dY W (TILE x
+    BLOCK on W^T) and wgrad dW = dY^T X (TILE x TILE).  Every buffer and event is allocated up
+    front.  streams=3: the casts, then the GEMMs, forked over three streams (default priority)
+    and joined by events, so that each GEMM's last partial round of tiles (896 tiles of 256 x
+    128 on 256 CUs: 3.5 rounds) overlaps the others."""
+
+    def __init__(self, sq, workloads, dev, streams=1):
+        import torch
+
+        self.sq = sq
+        TILE, BLOCK = sq.FP8_SCALE_TILE_1x128, sq.FP8_SCALE_BLOCK_128x128
+        X, W = (t.to(dev) for t in workloads.w3_inputs())
+        G = workloads.w3_grad().to(dev)
+        m, k = X.shape
+        n = W.shape[0]
+        u8 = dict(dtype=torch.uint8, device=dev)
+
+        def ct_out(rows, cols, gran):
+            qs, qts = ((cols // 128, rows), (rows // 128, cols)) if gran == TILE else \
+                ((rows // 128, cols // 128), (cols // 128, rows // 128))
+            return [torch.empty((rows, cols), **u8), torch.empty(qs, device=dev), torch.empty((cols, rows), **u8),
+                    torch.empty(qts, device=dev)]
+
+        self.casts = [(X, TILE, ct_out(m, k, TILE)), (W, BLOCK, ct_out(n, k, BLOCK)), (G, TILE, ct_out(m, n, TILE))]
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.Y, self.dX, self.dW = torch.empty((m, n), **bf), torch.empty((m, k), **bf), torch.empty((n, k), **bf)
+        self.flops = 3 * 2.0 * m * n * k
+        self.side = [torch.cuda.Stream(device=dev) for _ in range(2)] if streams == 3 else None
+        self.ev = [torch.cuda.Event() for _ in range(3)] if streams == 3 else None
+
+    def _cast(self, i):
+        x, gran, out = self.casts[i]
+        self.sq.fp8_cast_transpose_blockwise(x, self.sq.FP8_E4M3, gran, *out)
+
+    def _gemm(self, j):
+        sq = self.sq
+        TILE, BLOCK = sq.FP8_SCALE_TILE_1x128, sq.FP8_SCALE_BLOCK_128x128
+        (qx, sx, qxT, sxT), (qw, sw, qwT, swT), (qd, sd, qdT, sdT) = (c[2] for c in self.casts)
+        if j == 0:
+            sq.fp8_gemm(qx, 0, sx, TILE, qw, 0, sw, BLOCK, sq.OUT_BF16, C=self.Y)
+        elif j == 1:
+            sq.fp8_gemm(qd, 0, sd, TILE, qwT, 0, swT, BLOCK, sq.OUT_BF16, C=self.dX)
+        else:
+            sq.fp8_gemm(qdT, 0, sdT, TILE, qxT, 0, sxT, TILE, sq.OUT_BF16, C=self.dW)
+
+    def __call__(self):
+        if self.side is None:
+            for i in range(3):
+                self._cast(i)
+            for j in range(3):
+                self._gemm(j)
+            return
+        import torch
+
+        main = torch.cuda.current_stream()
+        s1, s2 = self.side
+        eX, eW, eD = self.ev
+        s1.wait_stream(main)
+        s2.wait_stream(main)
+        self._cast(0)
+        eX.record(main)
+        with torch.cuda.stream(s1):
+            self._cast(1)
+            eW.record(s1)
+        with torch.cuda.stream(s2):
+            self._cast(2)
+            eD.record(s2)
+        main.wait_event(eW)  # forward: X, W
+        self._gemm(0)
+        with torch.cuda.stream(s1):  # dgrad: dY, W^T
+            s1.wait_event(eD)
+            self._gemm(1)
+        with torch.cuda.stream(s2):  # wgrad: dY^T, X^T
+            s2.wait_event(eX)
+            self._gemm(2)
+        main.wait_stream(s1)
+        main.wait_stream(s2)
+
+    def outputs(self):
+        return [t for c in self.casts for t in c[2]] + [self.Y, self.dX, self.dW]
+
+
+def _step_timings(step, steps, warmup):
+    """(eager us, graph us) per step: launched call by call, and captured once as a graph."""
+    import torch
+
+    eager_us = _time_us(step, steps, warmup)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    return eager_us, _time_us(g.replay, steps, warmup)
 
 
 def blockwise_rows(sq, workloads, dev, steps, warmup):
@@ -475,6 +564,21 @@ def blockwise_rows(sq, workloads, dev, steps, warmup):
     mfma("gemm_wgrad_1x128_x_1x128",
          lambda: sq.fp8_gemm(og[0][2], 0, og[0][3], TILE, ox[0][2], 0, ox[0][3], TILE, sq.OUT_BF16, C=dW),
          2.0 * n * k * m)
+    del ox, ow, og, dX, dW
+    # the whole training step (three casts feeding three GEMMs), on one stream and on three
+    runs = {}
+    for streams in (1, 3):
+        st = BlockwiseStep(sq, workloads, dev, streams=streams)
+        e, g = _step_timings(st, steps, warmup)
+        name = "one stream" if streams == 1 else "three streams"
+        runs[name + ", eager"], runs[name + ", graph"] = e, g
+        flops = st.flops
+        del st
+    best = min(runs, key=runs.get)
+    out["step"] = {"what": "cast-transposes of X, W, dY feeding forward, dgrad and wgrad GEMMs (1.26e12 FLOP)",
+                   "us_per_step": round(runs[best], 2), "TFLOP/s": round(flops / runs[best] / 1e6, 1),
+                   "mfma_frac": round(flops / runs[best] / 1e6 / PEAK_FP8_TFLOPS, 4), "schedule": best,
+                   "us_per_step_by_schedule": {k: round(v, 2) for k, v in runs.items()}}
     return out
 
 

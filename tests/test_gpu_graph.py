@@ -1,7 +1,8 @@
 """Steps captured as HIP graphs: every replay must give exactly what the same steps give
 launched call by call.  Workload 2's step (MiniGPT layer set, delayed scaling, forward and
 backward: 9 cast-transposes, 9 GEMMs, the recipe update) on one stream and forked over three,
-and workload 1's 16-step loop (per-tensor quantize of X and W, GEMM, update).
+workload 1's 16-step loop (per-tensor quantize of X and W, GEMM, update), and workload 3's
+blockwise training step (3 blockwise cast-transposes, 3 GEMMs) on one stream and on three.
 
 The steps are the ones bench.py times.  Their entry points allocate nothing and record no
 memset, so every call goes into the graph.  The
@@ -95,5 +96,36 @@ def test_workload1_loop_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(_snapshot(step), eager[k])):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}: output {i} differs"
+        torch.ones(1 << 20, device=DEV).mul_(2.0).sum().item()
+
+
+@pytest.mark.parametrize("streams", [1, 3])
+def test_blockwise_step_graph_replays_match_eager(streams):
+    """Workload 3's blockwise training step (three blockwise cast-transposes feeding the forward,
+    dgrad and wgrad GEMMs), on one stream and forked over three: two graph replays, with eager
+    work between them, equal the eager step bit for bit (current scaling: no state between
+    steps)."""
+    import bench
+    import scaled_quantize_gemm_amd as sq
+    import workloads
+
+    announce("graph: blockwise step, eager reference, streams", streams)
+    step = bench.BlockwiseStep(sq, workloads, torch.device(DEV), streams=streams)
+    step()
+    torch.cuda.synchronize()
+    eager = _snapshot(step)
+    for t in step.outputs():  # the replays must rewrite every output
+        t.zero_()
+    announce("graph: blockwise capture, streams", streams)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for k in range(2):
+        announce("graph: blockwise replay", k, "streams", streams)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(_snapshot(step), eager)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {k}: output {i} differs"
         torch.ones(1 << 20, device=DEV).mul_(2.0).sum().item()
