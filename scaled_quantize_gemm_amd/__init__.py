@@ -95,7 +95,15 @@ def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+# the current stream's raw handle: torch's accessor takes ~0.1 us where building the Stream
+# object of torch.cuda.current_stream() takes ~2 us of a ~7 us call; the public route stays as
+# the fallback
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
