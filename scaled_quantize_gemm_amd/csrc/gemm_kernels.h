@@ -777,6 +777,9 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     for (int j = 0; j < NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i fa[4], fb[Shape::NT];
   float fsa[16], fsb[4] = {0.f, 0.f, 0.f, 0.f};
+  // the fold's scale factors for this K step: sa[row] * sb (block) in sc[0..15], or
+  // sa[row] * sb[column j] in sc[16 j + e] for two 1x128 operands
+  float sc[64];
   auto pack = [](const u32x4& lo, const u32x4& hi) -> v8i {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
@@ -827,17 +830,13 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       }
       return;
     } else {
-    float sab[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sab[e] = MODE == MODE_BLOCK ? fsa[e] * fsb[0] : fsa[e];
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     v4f p[16];
     auto fold = [&](int t) {
       const int i = t >> 2, j = t & 3;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        acc[i][j][jj] =
-            fmaf(p[t][jj], MODE == MODE_BLOCK ? sab[4 * jj + i] : sab[4 * jj + i] * fsb[j], acc[i][j][jj]);
+        acc[i][j][jj] = fmaf(p[t][jj], sc[(MODE == MODE_BLOCK ? 0 : 16 * j) + 4 * jj + i], acc[i][j][jj]);
     };
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -847,6 +846,19 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     }
     fold(14);
     fold(15);
+    }
+  };
+  // the scale products, formed while the other wave group runs its MFMAs, so that the fold
+  // in compute() is one FMA per accumulator
+  auto prep = [&]() {
+    if constexpr (MODE == MODE_BLOCK) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = fsa[e] * fsb[0];
+    } else if constexpr (MODE == MODE_TILE2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[16 * j + e] = fsa[e] * fsb[j];
     }
   };
   auto barrier = [&]() {
@@ -864,6 +876,11 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     __builtin_amdgcn_sched_barrier(0);
     if (STEADY || k + D < nk) issue(k + D, (ST + D) % NST);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (!TENSOR) {
+      __builtin_amdgcn_sched_barrier(0);
+      prep();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (STEADY) {
       wait_stage(1);  // this wave's part of stage k+1
     } else {
