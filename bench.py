@@ -27,6 +27,8 @@ Other lines, each printed instead of the main one:
   --minigpt     workload 2 (MiniGPT layer set, delayed scaling): the whole step on one and on
                 three streams, eager and as one captured graph
   --next-rows   workload 4's LayerNorm + cast and fused GEMM epilogues, and its backward GEMMs
+  --k-sweep     GEMM time against K for the three scalings at M x 7168 x K (cost per K step and
+                per tile of the blockwise kernel)
 """
 
 from __future__ import annotations
@@ -582,6 +584,48 @@ def blockwise_rows(sq, workloads, dev, steps, warmup):
     return out
 
 
+def k_sweep_rows(sq, workloads, dev, steps, warmup):
+    """GEMM time against K at fixed M, N for the three scalings (per tensor, 1x128 x 128x128,
+    1x128 x 1x128), bf16 out, on workload 3's operand distributions: the slope is the cost of
+    one 128-deep K step of the whole GEMM, the intercept the cost outside the K loop.  At
+    M = 2048, N = 7168 all three run on the 256 x 128 blockwise kernel (448 tiles); at
+    M = 4096 the per-tensor GEMM takes the 256 x 256 kernel."""
+    import torch
+
+    TENSOR, TILE, BLOCK = sq.FP8_SCALE_TENSOR, sq.FP8_SCALE_TILE_1x128, sq.FP8_SCALE_BLOCK_128x128
+    ks = (1024, 2048, 4096, 7168, 14336)
+    n = 7168
+    W = workloads.normal((n, ks[-1]), 0.02, 0, 302, torch.bfloat16).to(dev)
+    out = {"metric": "FP8 GEMM time against K (us), bf16 out", "steps": steps, "warmup": warmup,
+           "config": {"workload": "M x 7168 x K for M = 4096 and 2048, K = 1024 .. 14336; X ~ N(0, 1) with "
+                                  "0.1% outliers x100, W ~ N(0, 0.02); E4M3"},
+           "shapes": {}}
+    for m in (4096, 2048):
+        X = workloads.with_outliers(workloads.normal((m, ks[-1]), 1.0, 0, 300), 0.001, 100.0, 0, 301)
+        X = X.to(torch.bfloat16).to(dev)
+        C = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        rows = {"tensor": [], "tile_x_block": [], "tile_x_tile": []}
+        for k in ks:
+            x, w = X[:, :k].contiguous(), W[:, :k].contiguous()
+            qx, sx = sq.fp8_quantize(x, sq.FP8_E4M3, TILE)
+            qw, sw = sq.fp8_quantize(w, sq.FP8_E4M3, BLOCK)
+            qw1, sw1 = sq.fp8_quantize(w, sq.FP8_E4M3, TILE)
+            s_x = torch.tensor([448.0 / float(x.float().abs().max())], device=dev)
+            s_w = torch.tensor([448.0 / float(w.float().abs().max())], device=dev)
+            px, _ = sq.fp8_quantize(x, sq.FP8_E4M3, TENSOR, scale=s_x)
+            pw, _ = sq.fp8_quantize(w, sq.FP8_E4M3, TENSOR, scale=s_w)
+            ix, iw = s_x.reciprocal(), s_w.reciprocal()
+            rows["tensor"].append(round(_time_us(
+                lambda: sq.fp8_gemm(px, 0, ix, TENSOR, pw, 0, iw, TENSOR, sq.OUT_BF16, C=C), steps, warmup), 2))
+            rows["tile_x_block"].append(round(_time_us(
+                lambda: sq.fp8_gemm(qx, 0, sx, TILE, qw, 0, sw, BLOCK, sq.OUT_BF16, C=C), steps, warmup), 2))
+            rows["tile_x_tile"].append(round(_time_us(
+                lambda: sq.fp8_gemm(qx, 0, sx, TILE, qw1, 0, sw1, TILE, sq.OUT_BF16, C=C), steps, warmup), 2))
+        slope = {kind: round((t[-1] - t[-2]) / ((ks[-1] - ks[-2]) // 128), 3) for kind, t in rows.items()}
+        out["shapes"][f"{m}x{n}xK"] = {"K": list(ks), "us": rows, "us_per_k_step": slope}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -601,6 +645,9 @@ def main():
     ap.add_argument("--blockwise", action="store_true",
                     help="time workload 3's blockwise rows instead (1x128 / 128x128 quantizers and "
                          "cast-transposes, forward / dgrad / wgrad GEMMs); prints their own JSON line")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="time the GEMMs of the three scalings against K at M x 7168 x K (M = 4096, 2048); "
+                         "prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: runs on one GPU only; --gpus N with N > 1 is not supported (the library has no "
@@ -638,6 +685,10 @@ def main():
 
     if args.blockwise:
         print(json.dumps(blockwise_rows(sq, workloads, dev, args.steps, args.warmup)))
+        return
+
+    if args.k_sweep:
+        print(json.dumps(k_sweep_rows(sq, workloads, dev, args.steps, args.warmup)))
         return
 
     if args.next_rows:
