@@ -87,7 +87,7 @@ def test_tile_by_tile_gemm_small(sq, out, mnk):
 
 
 @pytest.mark.parametrize("out", [0, 1])
-@pytest.mark.parametrize("mnk", [(2085, 4100, 384), (2048, 4097, 1152), (1300, 3000, 128)])
+@pytest.mark.parametrize("mnk", [(2085, 4100, 384), (2048, 4097, 1152), (1300, 3000, 128), (300, 520, 14336)])
 def test_tile_by_tile_gemm_large(sq, out, mnk):
     M, N, K = mnk
     announce("large tile x tile gemm", out, mnk)

@@ -205,8 +205,8 @@ def test_large_tile_kernel(sq, mnk, mode):
 
 # Blockwise shapes with many 256 x 128 tiles on the large-tile blockwise kernel:
 # ragged M and N (N odd takes the unpaired epilogue), K steps fewer than and not a multiple
-# of the pipeline depth.
-BIG_BLOCK_CASES = [(2085, 4100, 384), (2048, 4097, 1152), (4096, 2304, 256), (1300, 3000, 128)]
+# of the pipeline depth, and a long K (112 steps).
+BIG_BLOCK_CASES = [(2085, 4100, 384), (2048, 4097, 1152), (4096, 2304, 256), (1300, 3000, 128), (300, 520, 14336)]
 
 
 @pytest.mark.parametrize("out", [0, 1])
