@@ -95,6 +95,72 @@ def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _need(t: Optional[torch.Tensor], name: str, dtype, shape=None, min_numel: Optional[int] = None,
+          device=None) -> None:
+    """A caller-supplied buffer: contiguous, of `dtype`, and of exactly `shape` (or at least
+    `min_numel` elements).  The C side sees only pointers, so a mis-sized buffer would be read
+    or written out of bounds on the device.  Where each tensor lives is checked afterwards,
+    for all of a call's tensors at once (_on_device)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} element(s), got {t.numel()}")
+
+
+def _on_device(**named) -> None:
+    """Every given tensor on the same GPU (the first one's)."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call's other tensors on {dev}")
+
+
+def _scale_shape(gran: int, rows: int, k: int, operand_b: bool):
+    """(dtype, shape) of a GEMM operand's scales in the layouts of scaled_fp8.h."""
+    if gran == FP8_SCALE_TENSOR:
+        return torch.float32, None
+    if gran == FP8_SCALE_TILE_1x128:
+        return torch.float32, (k // 128, rows)
+    if gran == FP8_SCALE_BLOCK_128x128:
+        return torch.float32, ((rows + 127) // 128, k // 128)
+    if gran == FP8_SCALE_MX_1x32:
+        return torch.uint8, (k // 32, rows)
+    raise ValueError(f"unknown granularity {gran}")
+
+
+def _gemm_operands(A, a_scale_inv, gran_a, B, b_scale_inv, gran_b):
+    _need(A, "A", torch.uint8)
+    _need(B, "B", torch.uint8)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: {K} vs {K2}")
+    for t, nm, g, rows, isb in ((a_scale_inv, "a_scale_inv", gran_a, M, False),
+                                (b_scale_inv, "b_scale_inv", gran_b, N, True)):
+        if t is None:
+            raise ValueError(f"{nm} is required")
+        dt, shp = _scale_shape(g, rows, K, isb)
+        _need(t, nm, dt, shape=shp, min_numel=1 if shp is None else None)
+    return M, N, K
+
+
 # the current stream's raw handle: torch's accessor takes ~0.1 us where building the Stream
 # object of torch.cuda.current_stream() takes ~2 us of a ~7 us call; the public route stays as
 # the fallback
@@ -123,6 +189,8 @@ def _as2d(x: torch.Tensor):
     return x.shape[0], x.shape[1]
 
 
+_OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_E4M3: torch.uint8, OUT_E5M2: torch.uint8}
+
 # ------------------------------------------------------------------ entry points
 
 
@@ -136,13 +204,15 @@ def fp8_device_check(device: int = 0):
 def fp8_recipe_update(amax_history: torch.Tensor, scale: torch.Tensor, scale_inv: torch.Tensor, fmts: List[int],
                       margin: int = 0, algo: int = FP8_AMAX_ALGO_MAX) -> None:
     """End-of-step delayed-scaling update of [H][n] history and [n] scales (in place)."""
+    _need(amax_history, "amax_history", torch.float32)
+    if amax_history.dim() != 2:
+        raise ValueError("amax_history must be [H][n]")
     h, n = amax_history.shape
-    for t, nm in ((amax_history, "amax_history"), (scale, "scale"), (scale_inv, "scale_inv")):
-        _contig(t, nm)
-        if t.dtype != torch.float32:
-            raise TypeError(f"{nm} must be float32")
-    if scale.numel() != n or scale_inv.numel() != n or len(fmts) != n:
-        raise ValueError("scale, scale_inv and fmts must have n entries")
+    _need(scale, "scale", torch.float32, shape=(n,))
+    _need(scale_inv, "scale_inv", torch.float32, shape=(n,))
+    if len(fmts) != n:
+        raise ValueError("fmts must have n entries")
+    _on_device(amax_history=amax_history, scale=scale, scale_inv=scale_inv)
     arr = (ctypes.c_int * n)(*fmts)
     _check(lib.fp8_recipe_update(_ptr(amax_history), _ptr(scale), _ptr(scale_inv), arr, n, h, algo, margin,
                                  _stream(amax_history)))
@@ -152,8 +222,19 @@ def fp8_quantize(x: torch.Tensor, fmt: int, granularity: int = FP8_SCALE_TENSOR,
                  amax_slot: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
                  scale_inv_out: Optional[torch.Tensor] = None):
     """Fused amax + cast of x [rows][cols] -> (q uint8 [rows][cols], scale_inv_out or None)."""
-    _contig(x, "x")
+    _need(x, "x", (torch.bfloat16, torch.float32))
     rows, cols = _as2d(x)
+    _need(q, "q", torch.uint8, shape=tuple(x.shape))
+    _need(scale, "scale", torch.float32, min_numel=1)
+    _need(amax_slot, "amax_slot", torch.float32, min_numel=1)
+    if scale_inv_out is not None:
+        if granularity == FP8_SCALE_TILE_1x128:
+            _need(scale_inv_out, "scale_inv_out", torch.float32, shape=(cols // 128, rows))
+        elif granularity == FP8_SCALE_BLOCK_128x128:
+            _need(scale_inv_out, "scale_inv_out", torch.float32, shape=((rows + 127) // 128, cols // 128))
+        elif granularity == FP8_SCALE_MX_1x32:
+            _need(scale_inv_out, "scale_inv_out", torch.uint8, shape=(cols // 32, rows))
+    _on_device(x=x, q=q, scale=scale, amax_slot=amax_slot, scale_inv_out=scale_inv_out)
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scale_inv_out is None and granularity != FP8_SCALE_TENSOR:
@@ -172,10 +253,13 @@ def fp8_quantize_diag(x: torch.Tensor, fmt: int, scale: torch.Tensor, counts: to
                       amax_slot: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-tensor cast with diagnostics: adds (saturated, underflowed, nan) element counts to
     `counts` (device int64 [3]); returns q."""
-    _contig(x, "x")
+    _need(x, "x", (torch.bfloat16, torch.float32))
     rows, cols = _as2d(x)
-    if counts.dtype != torch.int64 or counts.numel() != 3:
-        raise TypeError("counts must be a device int64 tensor of 3 entries")
+    _need(counts, "counts", torch.int64, shape=(3,))
+    _need(scale, "scale", torch.float32, min_numel=1)
+    _need(amax_slot, "amax_slot", torch.float32, min_numel=1)
+    _need(q, "q", torch.uint8, shape=(rows, cols))
+    _on_device(x=x, counts=counts, scale=scale, amax_slot=amax_slot, q=q)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     _check(lib.fp8_quantize_diag(_ptr(x), _hp_dtype(x), rows, cols, fmt, _ptr(scale), _ptr(amax_slot), _ptr(q),
@@ -186,8 +270,13 @@ def fp8_quantize_diag(x: torch.Tensor, fmt: int, scale: torch.Tensor, counts: to
 def fp8_cast_transpose(x: torch.Tensor, fmt: int, scale: torch.Tensor, amax_slot: Optional[torch.Tensor] = None,
                        q: Optional[torch.Tensor] = None, qT: Optional[torch.Tensor] = None):
     """Per-tensor cast of x [rows][cols] and its transpose -> (q [rows][cols], qT [cols][rows])."""
-    _contig(x, "x")
+    _need(x, "x", (torch.bfloat16, torch.float32))
     rows, cols = _as2d(x)
+    _need(scale, "scale", torch.float32, min_numel=1)
+    _need(amax_slot, "amax_slot", torch.float32, min_numel=1)
+    _need(q, "q", torch.uint8, shape=(rows, cols))
+    _need(qT, "qT", torch.uint8, shape=(cols, rows))
+    _on_device(x=x, scale=scale, amax_slot=amax_slot, q=q, qT=qT)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if qT is None:
@@ -204,17 +293,22 @@ def fp8_cast_transpose_blockwise(x: torch.Tensor, fmt: int, granularity: int, q:
     (q [rows][cols], q_scale_inv, qT [cols][rows], qT_scale_inv).  TILE_1x128: q_scale_inv
     [cols/128][rows], qT_scale_inv [rows/128][cols]; BLOCK_128x128: [rows/128][cols/128] and
     its transpose."""
-    _contig(x, "x")
+    _need(x, "x", (torch.bfloat16, torch.float32))
     rows, cols = _as2d(x)
     dev = x.device
-    if q is None:
-        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    if qT is None:
-        qT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
     if granularity == FP8_SCALE_TILE_1x128:
         qs, qts = (cols // 128, rows), (rows // 128, cols)
     else:
         qs, qts = (rows // 128, cols // 128), (cols // 128, rows // 128)
+    _need(q, "q", torch.uint8, shape=(rows, cols))
+    _need(qT, "qT", torch.uint8, shape=(cols, rows))
+    _need(q_scale_inv, "q_scale_inv", torch.float32, shape=qs)
+    _need(qT_scale_inv, "qT_scale_inv", torch.float32, shape=qts)
+    _on_device(x=x, q=q, qT=qT, q_scale_inv=q_scale_inv, qT_scale_inv=qT_scale_inv)
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if qT is None:
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
     if q_scale_inv is None:
         q_scale_inv = torch.empty(qs, dtype=torch.float32, device=dev)
     if qT_scale_inv is None:
@@ -228,15 +322,13 @@ def fp8_gemm(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_a: int
              b_scale_inv: torch.Tensor, gran_b: int, out_dtype: int = OUT_F32,
              C: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C[M][N] = deq(A)[M][K] . deq(B)[N][K]^T."""
-    _contig(A, "A")
-    _contig(B, "B")
-    M, K = A.shape
-    N, K2 = B.shape
-    if K != K2:
-        raise ValueError(f"K mismatch: {K} vs {K2}")
+    M, N, K = _gemm_operands(A, a_scale_inv, gran_a, B, b_scale_inv, gran_b)
+    if out_dtype not in (OUT_F32, OUT_BF16):
+        raise ValueError(f"out_dtype {out_dtype}: fp8_gemm writes OUT_F32 or OUT_BF16")
+    _need(C, "C", _OUT_TORCH[out_dtype], shape=(M, N))
+    _on_device(A=A, B=B, a_scale_inv=a_scale_inv, b_scale_inv=b_scale_inv, C=C)
     if C is None:
-        dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
-        C = torch.empty((M, N), dtype=dt, device=A.device)
+        C = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=A.device)
     _check(lib.fp8_gemm(_ptr(A), fmt_a, _ptr(a_scale_inv), gran_a, _ptr(B), fmt_b, _ptr(b_scale_inv), gran_b,
                         _ptr(C), out_dtype, M, N, K, _stream(A)))
     return C
@@ -248,13 +340,23 @@ def fp8_layernorm_quantize(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[
                            scale_inv_out: Optional[torch.Tensor] = None, mu: Optional[torch.Tensor] = None,
                            rsigma: Optional[torch.Tensor] = None):
     """LayerNorm over the last dim of x [rows][cols] cast to FP8 -> (q, scale_inv_out or None)."""
-    _contig(x, "x")
-    _contig(gamma, "gamma")
+    _need(x, "x", (torch.bfloat16, torch.float32))
     rows, cols = _as2d(x)
+    _need(gamma, "gamma", (torch.bfloat16, torch.float32), shape=(cols,))
     if beta is not None:
-        _contig(beta, "beta")
-        if beta.dtype != gamma.dtype:
-            raise TypeError("gamma and beta must share a dtype")
+        _need(beta, "beta", gamma.dtype, shape=(cols,))
+    _need(q, "q", torch.uint8, shape=(rows, cols))
+    _need(scale, "scale", torch.float32, min_numel=1)
+    _need(amax_slot, "amax_slot", torch.float32, min_numel=1)
+    _need(mu, "mu", torch.float32, shape=(rows,))
+    _need(rsigma, "rsigma", torch.float32, shape=(rows,))
+    if scale_inv_out is not None:
+        if granularity == FP8_SCALE_TILE_1x128:
+            _need(scale_inv_out, "scale_inv_out", torch.float32, shape=(cols // 128, rows))
+        elif granularity == FP8_SCALE_MX_1x32:
+            _need(scale_inv_out, "scale_inv_out", torch.uint8, shape=(cols // 32, rows))
+    _on_device(x=x, gamma=gamma, beta=beta, q=q, scale=scale, amax_slot=amax_slot, mu=mu, rsigma=rsigma,
+               scale_inv_out=scale_inv_out)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale_inv_out is None and granularity == FP8_SCALE_TILE_1x128:
@@ -267,9 +369,6 @@ def fp8_layernorm_quantize(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[
     return q, scale_inv_out
 
 
-_OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_E4M3: torch.uint8, OUT_E5M2: torch.uint8}
-
-
 def fp8_gemm_fused(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_a: int, B: torch.Tensor, fmt_b: int,
                    b_scale_inv: torch.Tensor, gran_b: int, out_dtype: int = OUT_BF16,
                    bias: Optional[torch.Tensor] = None, act: int = FP8_ACT_NONE, aux: Optional[torch.Tensor] = None,
@@ -277,18 +376,23 @@ def fp8_gemm_fused(A: torch.Tensor, fmt_a: int, a_scale_inv: torch.Tensor, gran_
                    C: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp8_gemm with bias, optional bf16 pre-activation copy (aux), GELU / SwiGLU and an
     fp32 / bf16 / FP8 output (FP8: codes under c_scale, amax max-reduced into c_amax)."""
-    _contig(A, "A")
-    _contig(B, "B")
-    M, K = A.shape
-    N, K2 = B.shape
-    if K != K2:
-        raise ValueError(f"K mismatch: {K} vs {K2}")
+    M, N, K = _gemm_operands(A, a_scale_inv, gran_a, B, b_scale_inv, gran_b)
+    dev = A.device
+    if out_dtype not in _OUT_TORCH:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
+    cols = N // 2 if act == FP8_ACT_SWIGLU else N
+    _need(C, "C", _OUT_TORCH[out_dtype], shape=(M, cols))
+    _need(aux, "aux", torch.bfloat16, shape=(M, N))
+    _need(bias, "bias", (torch.float32, torch.bfloat16), shape=(N,))
+    if out_dtype in (OUT_E4M3, OUT_E5M2):
+        _need(c_scale, "c_scale", torch.float32, min_numel=1)
+        _need(c_amax, "c_amax", torch.float32, min_numel=1)
+    _on_device(A=A, B=B, a_scale_inv=a_scale_inv, b_scale_inv=b_scale_inv, C=C, aux=aux, bias=bias, c_scale=c_scale,
+               c_amax=c_amax)
     if C is None:
-        cols = N // 2 if act == FP8_ACT_SWIGLU else N
-        C = torch.empty((M, cols), dtype=_OUT_TORCH.get(out_dtype, torch.float32), device=A.device)
+        C = torch.empty((M, cols), dtype=_OUT_TORCH[out_dtype], device=dev)
     bias_dt = HP_F32
     if bias is not None:
-        _contig(bias, "bias")
         bias_dt = _hp_dtype(bias)
     _check(lib.fp8_gemm_fused(_ptr(A), fmt_a, _ptr(a_scale_inv), gran_a, _ptr(B), fmt_b, _ptr(b_scale_inv), gran_b,
                               _ptr(bias), bias_dt, act, _ptr(aux), _ptr(C), out_dtype, _ptr(c_scale), _ptr(c_amax),

@@ -23,3 +23,9 @@ def read_golden(name):
             if line:
                 rows.append([c.strip() for c in line.split("|")])
     return rows
+
+
+def pytest_sessionfinish(session, exitstatus):
+    mod = sys.modules.get("gpu_util")
+    if mod is not None:
+        mod.write_tolerance_stats()

@@ -2,6 +2,9 @@
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import json
+import os
 import sys
 
 import numpy as np
@@ -10,6 +13,26 @@ import torch
 from oracle import fp8 as ofp8
 
 DEV = "cuda:0"
+
+# per-case statistics against the stated GEMM tolerance, written out at the end of the session
+TOLERANCE_STATS = {}
+OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+
+
+def write_tolerance_stats(name="gemm_tolerance_workloads.json") -> None:
+    if TOLERANCE_STATS:
+        os.makedirs(OUT_DIR, exist_ok=True)
+        with open(os.path.join(OUT_DIR, name), "w") as f:
+            json.dump(TOLERANCE_STATS, f, indent=1, sort_keys=True)
+
+
+def par_rows(fn, x, *args, chunks=16):
+    """fn(x[rows], *args) over row chunks in threads (the oracle's elementwise quantisers
+    release the interpreter lock); returns the list of per-chunk results in row order."""
+    n = x.shape[0]
+    edges = np.linspace(0, n, min(chunks, n) + 1).astype(int)
+    with cf.ThreadPoolExecutor(max_workers=min(16, len(edges) - 1)) as ex:
+        return list(ex.map(lambda i: fn(x[edges[i]:edges[i + 1]], *args), range(len(edges) - 1)))
 
 
 def announce(*what) -> None:
@@ -65,6 +88,7 @@ def check_gemm(C_gpu, C_ref, S, G, K, mode, out_bf16, label=""):
     stats = {"max_err_over_S": float(rel.max()), "frac_within_2^-18_S": frac_ns,
              "max_err_over_bound": float((err / np.where(bound > 0, bound, 1.0)).max())}
     print(f"[gemm] {label} {stats}", flush=True)
+    TOLERANCE_STATS[label] = stats
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{label}: {int(bad.sum())} outputs beyond bound; first {tuple(i)}: gpu={C_gpu[tuple(i)]} "

@@ -163,3 +163,107 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert p.returncode != 0
     assert "one GPU" in p.stderr
+
+
+# ------------------------------------------------------------------ binding buffer checks
+#
+# The C side sees only pointers, so the binding checks every caller-supplied tensor's dtype,
+# shape and contiguity, then that all of a call's tensors are on one GPU, before anything
+# reaches the library.  On the CPU every check runs in that order: a mis-sized buffer raises
+# its own error; correctly sized host tensors end at the device check.
+
+
+def _e(*shape, dtype=None):
+    import torch
+
+    return torch.empty(shape, dtype=dtype or torch.float32)
+
+
+def _raises(fn, exc, match):
+    with pytest.raises(exc, match=match):
+        fn()
+
+
+def test_gemm_rejects_mis_sized_buffers():
+    import torch
+
+    import scaled_quantize_gemm_amd as sq
+
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    M, N, K = 64, 48, 256
+    A, B = _e(M, K, dtype=u8), _e(N, K, dtype=u8)
+    one = _e(1)
+    g = sq.fp8_gemm
+    _raises(lambda: g(A.float(), 0, one, 0, B, 0, one, 0), TypeError, "A must be")
+    _raises(lambda: g(A, 0, one, 0, _e(N, K + 128, dtype=u8), 0, one, 0), ValueError, "K mismatch")
+    _raises(lambda: g(A, 0, one, 0, B, 0, one, 0, sq.OUT_F32, C=_e(M, N, dtype=bf)), TypeError, "C must be")
+    _raises(lambda: g(A, 0, one, 0, B, 0, one, 0, sq.OUT_BF16, C=_e(M, N - 1, dtype=bf)), ValueError, "C must have")
+    _raises(lambda: g(A, 0, one, 0, B, 0, one, 0, sq.OUT_F32, C=_e(N, M).t()), ValueError, "contiguous")
+    _raises(lambda: g(A, 0, _e(0), 0, B, 0, one, 0), ValueError, "at least 1")
+    _raises(lambda: g(A, 0, one.double(), 0, B, 0, one, 0), TypeError, "a_scale_inv must be")
+    # TILE x BLOCK: [K/128][M] and [ceil(N/128)][K/128]
+    sa, sb = _e(K // 128, M), _e(1, K // 128)
+    _raises(lambda: g(A, 0, _e(K // 128, M - 1), 1, B, 0, sb, 2), ValueError, "a_scale_inv must have")
+    _raises(lambda: g(A, 0, sa, 1, B, 0, _e(K // 128, 1), 2), ValueError, "b_scale_inv must have")
+    # TILE x TILE: B's scales [K/128][N]
+    _raises(lambda: g(A, 0, sa, 1, B, 0, _e(K // 128, N + 1), 1), ValueError, "b_scale_inv must have")
+    # MX: uint8 [K/32][rows]
+    _raises(lambda: g(A, 0, _e(K // 32, M), 3, B, 0, _e(K // 32, N, dtype=u8), 3), TypeError, "a_scale_inv must be")
+    _raises(lambda: g(A, 0, _e(M, K // 32, dtype=u8), 3, B, 0, _e(K // 32, N, dtype=u8), 3), ValueError,
+            "a_scale_inv must have")
+    _raises(lambda: g(A, 0, one, 0, B, 0, one, 0, sq.OUT_E4M3), ValueError, "OUT_F32 or OUT_BF16")
+    # every size right: the host tensors stop at the device check
+    _raises(lambda: g(A, 0, sa, 1, B, 0, sb, 2, sq.OUT_BF16, C=_e(M, N, dtype=bf)), ValueError, "GPU tensor")
+
+
+def test_fused_gemm_rejects_mis_sized_buffers():
+    import torch
+
+    import scaled_quantize_gemm_amd as sq
+
+    u8, bf = torch.uint8, torch.bfloat16
+    M, N, K = 32, 64, 128
+    A, B, one = _e(M, K, dtype=u8), _e(N, K, dtype=u8), _e(1)
+    f = sq.fp8_gemm_fused
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_BF16, act=sq.FP8_ACT_SWIGLU, C=_e(M, N, dtype=bf)),
+            ValueError, "C must have")
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_E4M3, C=_e(M, N, dtype=bf)), TypeError, "C must be")
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_BF16, aux=_e(M, N)), TypeError, "aux must be")
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_BF16, aux=_e(M, N // 2, dtype=bf)), ValueError,
+            "aux must have")
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_BF16, bias=_e(N + 1)), ValueError, "bias must have")
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_E4M3, c_scale=_e(0), c_amax=one), ValueError, "at least 1")
+    _raises(lambda: f(A, 0, one, 0, B, 0, one, 0, sq.OUT_E4M3, c_scale=one, c_amax=one), ValueError, "GPU tensor")
+
+
+def test_casts_reject_mis_sized_buffers():
+    import torch
+
+    import scaled_quantize_gemm_amd as sq
+
+    u8, bf, f32 = torch.uint8, torch.bfloat16, torch.float32
+    x = _e(256, 384, dtype=bf)
+    one = _e(1)
+    _raises(lambda: sq.fp8_quantize(x.half(), 0), TypeError, "x must be")
+    _raises(lambda: sq.fp8_quantize(x, 0, q=_e(256, 383, dtype=u8)), ValueError, "q must have")
+    _raises(lambda: sq.fp8_quantize(x, 0, 1, scale_inv_out=_e(256, 3)), ValueError, "scale_inv_out must have")
+    _raises(lambda: sq.fp8_quantize(x, 0, 2, scale_inv_out=_e(3, 2)), ValueError, "scale_inv_out must have")
+    _raises(lambda: sq.fp8_quantize(x, 0, 3, scale_inv_out=_e(12, 256)), TypeError, "scale_inv_out must be")
+    _raises(lambda: sq.fp8_quantize(x, 0, 0, scale=_e(1, dtype=bf)), TypeError, "scale must be")
+    _raises(lambda: sq.fp8_quantize(x, 0, 0, scale=one, amax_slot=_e(0)), ValueError, "at least 1")
+    _raises(lambda: sq.fp8_quantize(x, 0, 0, scale=one), ValueError, "GPU tensor")
+    _raises(lambda: sq.fp8_quantize_diag(x, 0, one, _e(2, dtype=torch.int64)), ValueError, "counts must have")
+    _raises(lambda: sq.fp8_cast_transpose(x, 0, one, qT=_e(256, 384, dtype=u8)), ValueError, "qT must have")
+    _raises(lambda: sq.fp8_cast_transpose(x, 0, one, q=_e(384, 256, dtype=u8)), ValueError, "q must have")
+    _raises(lambda: sq.fp8_cast_transpose_blockwise(x, 0, 1, q_scale_inv=_e(2, 256)), ValueError,
+            "q_scale_inv must have")
+    _raises(lambda: sq.fp8_cast_transpose_blockwise(x, 0, 2, qT_scale_inv=_e(2, 3)), ValueError,
+            "qT_scale_inv must have")
+    g = _e(384, dtype=bf)
+    _raises(lambda: sq.fp8_layernorm_quantize(x, _e(383, dtype=bf), None, 1e-5, 0), ValueError, "gamma must have")
+    _raises(lambda: sq.fp8_layernorm_quantize(x, g, _e(384), 1e-5, 0), TypeError, "beta must be")
+    _raises(lambda: sq.fp8_layernorm_quantize(x, g, None, 1e-5, 0, mu=_e(255)), ValueError, "mu must have")
+    _raises(lambda: sq.fp8_layernorm_quantize(x, g, None, 1e-5, 0, 1, scale_inv_out=_e(3, 255)), ValueError,
+            "scale_inv_out must have")
+    _raises(lambda: sq.fp8_recipe_update(_e(16, 3), _e(2), _e(3), [0, 0, 1]), ValueError, "scale must have")
+    _raises(lambda: sq.fp8_recipe_update(_e(16, 3), _e(3), _e(3), [0, 0, 1]), ValueError, "GPU tensor")

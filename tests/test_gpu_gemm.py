@@ -278,3 +278,47 @@ def test_all_maximum_codes_sum_exactly(sq, M, N):
     row_sign = np.where(np.arange(M) % 2 == 1, -1.0, 1.0)[:, None]
     want = row_sign * 200704.0 * (K - 2 * (K // 4)) * np.ones((1, N))
     assert np.array_equal(np_of(C), want.astype(np.float32))
+
+
+def _ieee_rows(Ad, Bd, rows):
+    """The definition's sums for the given rows, elementwise in float64 (IEEE: a NaN product,
+    inf x 0 or inf - inf give NaN)."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        return np.stack([np.sum(Ad[m][None, :] * Bd, axis=1) for m in rows])
+
+
+@pytest.mark.parametrize("route", [("large", 4096, 4096), ("narrow", 256, 512), ("small", 2, 96)])
+def test_nan_inf_codes_propagate(sq, route):
+    """E5M2 infinities and NaN codes in A, E4M3 NaN codes and zero columns in B: outputs are
+    NaN exactly where the definition's sum is NaN and +-inf where it is +-inf."""
+    name, M, N = route
+    K = 256
+    announce("nan/inf codes", name, (M, N, K))
+    rng = np.random.default_rng(404)
+    A = _codes(rng, (M, K), 1)  # E5M2
+    B = _codes(rng, (N, K), 0)  # E4M3
+    PINF, NINF, NAN5, NAN4 = 0x7C, 0xFC, 0x7F, 0x7F
+    rows = np.arange(min(M, 48))
+    for m in rows:
+        kind, k = m % 6, (m * 37) % K
+        if kind == 0:
+            A[m, k] = NAN5
+        elif kind == 1:
+            A[m, k] = PINF
+        elif kind == 2:
+            A[m, k] = NINF
+        elif kind == 3:
+            A[m, k], A[m, (k + 100) % K] = PINF, NINF
+        elif kind == 4:
+            A[m, k], A[m, (k + 9) % K] = PINF, PINF
+    B[::5, :] = np.where(np.arange(K)[None, :] % 37 == 0, 0, B[::5, :])  # zeros under some infinities
+    B[3 % N, 11] = NAN4
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    C = np_of(sq.fp8_gemm(_t(A), 1, _scal(sa), 0, _t(B), 0, _scal(sb), 0, sq.OUT_F32))[rows].astype(np.float64)
+    torch.cuda.synchronize()
+    want = _ieee_rows(og.dequant(A, 1, og.TENSOR, sa), og.dequant(B, 0, og.TENSOR, sb), rows)
+    assert np.isnan(want).any() and np.isinf(want).any()
+    assert np.array_equal(np.isnan(C), np.isnan(want)), f"{name}: NaN positions differ"
+    inf = np.isinf(want)
+    assert np.array_equal(np.isinf(C), inf) and np.array_equal(np.sign(C[inf]), np.sign(want[inf])), \
+        f"{name}: infinities differ"

@@ -207,8 +207,9 @@ def test_fused_argument_errors(sq):
     B5 = torch.zeros((5, 128), dtype=torch.uint8, device=DEV)
     one = _scal(1.0)
     with pytest.raises(sq.Fp8Error) as e:
+        # the binding takes C as [M][N // 2]; the library rejects the odd N
         sq.fp8_gemm_fused(A, 0, one, 0, B5, 0, one, 0, out_dtype=sq.OUT_F32, act=sq.FP8_ACT_SWIGLU,
-                          C=torch.empty((4, 3), device=DEV))
+                          C=torch.empty((4, 2), device=DEV))
     assert e.value.code == sq.FP8_ERR_SHAPE
     with pytest.raises(sq.Fp8Error) as e:
         sq.fp8_gemm_fused(A, 0, one, 0, B, 0, one, 0, out_dtype=sq.OUT_E4M3)  # no c_scale / c_amax
