@@ -47,7 +47,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mx_8192_traffic.json")
 # the sources each kernel is built from (a counter summary is current only for these)
-GEMM_SOURCES = ["gemm.hip", "gemm_kernels.h", "gemm_epilogue.h", "common.h"]
+GEMM_SOURCES = ["gemm_pp.h", "gemm_common.h", "gemm_epilogue.h", "common.h"]  # the MX GEMM's kernel and launch
 QUANT_SOURCES = ["quantize.hip", "quant_rules.h", "common.h"]
 CT_SOURCES = ["cast_transpose.hip", "quant_rules.h", "common.h"]
 
@@ -60,24 +60,97 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key, sources):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+def _counters(kernel_key, sources):
+    """The committed rocprofv3 counter summary of a kernel, if its sources are unchanged since."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     e = d.get(kernel_key)
     if not e or e.get("source_sha") != _src_hash(*sources):
-        return None
-    return e.get("traffic_bytes")
+        return {}
+    return e
 
 
-def cpu_baseline(M=8192, K=8192, numel=1 << 28, rows=4096, stream_sample=1 << 26):
-    """The oracle as it stands, on a bounded sample of the same workload (host cores)."""
-    import numpy as np
-    import torch
+def _traffic(kernel_key, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+    return _counters(kernel_key, sources).get("traffic_bytes")
+
+
+def _blas_threads():
     from threadpoolctl import threadpool_info
+
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return int(max(blas) if blas else 1)
+
+
+def _seconds(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return time.perf_counter() - t0, r
+
+
+def _one_thread(fn):
+    """fn() with the BLAS pool limited to one thread (NumPy's elementwise work is single-threaded)."""
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        return _seconds(fn)
+
+
+def _host_info():
+    return {"host_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def oracle_single_thread_parts():
+    """The oracle's GEMM on one BLAS thread at workloads 1-3 (workload 3 on a row sample) and its
+    cast-transpose on a row sample of workload 4's gradient, single-threaded like all its casts."""
+    import numpy as np
+
+    import workloads
+    from oracle import gemm as og, quantize as oq
+
+    out = {}
+    # workload 1: 256^3 per tensor
+    x, w = workloads.w1_input(0).numpy(), workloads.w1_weight().numpy()
+    qx = oq.quantize_tensor(x, np.float32(448 / np.abs(x).max()), 0)[0]
+    qw = oq.quantize_tensor(w, np.float32(448 / np.abs(w).max()), 0)[0]
+    dt, _ = _one_thread(lambda: og.gemm_ref(qx, 0, np.float32(1), og.TENSOR, qw, 0, np.float32(1), og.TENSOR))
+    out["workload1_gemm_256^3"] = {"seconds": round(dt, 4), "gflop_s": round(2 * 256 ** 3 / dt / 1e9, 2)}
+    # workload 2: the QKV forward GEMM 2048 x 2304 x 768
+    X, W, _ = workloads.w2_layer(0, 0)
+    x, w = X.float().numpy(), W.float().numpy()
+    qx = oq.quantize_tensor(x, np.float32(448 / np.abs(x).max()), 0)[0]
+    qw = oq.quantize_tensor(w, np.float32(448 / np.abs(w).max()), 0)[0]
+    dt, _ = _one_thread(lambda: og.gemm_ref(qx, 0, np.float32(1), og.TENSOR, qw, 0, np.float32(1), og.TENSOR))
+    out["workload2_qkv_gemm_2048x2304x768"] = {"seconds": round(dt, 3),
+                                               "gflop_s": round(2 * 2048 * 2304 * 768 / dt / 1e9, 2)}
+    # workload 3: 128 rows of the blockwise GEMM 4096 x 7168 x 7168
+    X, W = workloads.w3_inputs()
+    qx, sx = oq.quantize_tile_1x128(X[:128].float().numpy(), 0)
+    w = W.float().numpy()
+    dq, _ = _seconds(lambda: oq.quantize_block_128x128(w[:1024], 0))
+    qw, sw = oq.quantize_block_128x128(w, 0)
+    dt, _ = _one_thread(lambda: og.gemm_ref(qx, 0, sx, og.TILE_1x128, qw, 0, sw, og.BLOCK_128x128))
+    out["workload3_blockwise_gemm_128x7168x7168"] = {"seconds": round(dt, 3),
+                                                     "gflop_s": round(2 * 128 * 7168 * 7168 / dt / 1e9, 2)}
+    out["workload3_quantize_128x128_1024x7168"] = {"seconds": round(dq, 3),
+                                                   "gb_s": round(1024 * 7168 * 3 / dq / 1e9, 3)}
+    # workload 4: cast-transpose of 512 rows of dY [8192 x 14336]
+    d = workloads.w4_inputs()[2][:512].float().numpy()
+    dt, _ = _seconds(lambda: oq.cast_transpose(d, np.float32(57344 / 5e-4), 1))
+    out["workload4_cast_transpose_512x14336"] = {"seconds": round(dt, 3), "gb_s": round(d.size * 4 / dt / 1e9, 3)}
+    return out
+
+
+def cpu_baseline(M=8192, K=8192, rows=4096, stream_sample=1 << 26):
+    """The oracle as it stands, on a bounded sample of the bench step (host cores): MX quantize of
+    A[:rows] and B[:rows], its fp64 GEMM (C, with the bound matrices S and G it computes
+    alongside) on all BLAS threads, and the per-tensor cast of the first `stream_sample` stream
+    elements.  value = the sample's GEMM FLOPs / the sample's oracle time (the bench's own
+    definition of a step's throughput).  Returns (summary, arrays for the parity check)."""
+    import numpy as np
 
     import workloads
     from oracle import gemm as og, quantize as oq
@@ -87,22 +160,61 @@ def cpu_baseline(M=8192, K=8192, numel=1 << 28, rows=4096, stream_sample=1 << 26
     b = B[:rows].float().numpy()
     t = workloads.w5_stream(numel=stream_sample).float().numpy()
     del A, B
-    t0 = time.perf_counter()
-    qa, ea = oq.quantize_mx_1x32(a, 0)
-    qb, eb = oq.quantize_mx_1x32(b, 0)
-    C, _, _ = og.gemm_ref(qa, 0, ea, og.MX_1x32, qb, 0, eb, og.MX_1x32)
+    dq, ((qa, ea), (qb, eb)) = _seconds(lambda: (oq.quantize_mx_1x32(a, 0), oq.quantize_mx_1x32(b, 0)))
+    dg, (C, S, G) = _seconds(lambda: og.gemm_ref(qa, 0, ea, og.MX_1x32, qb, 0, eb, og.MX_1x32))
     C16 = og.to_bf16(C.astype(np.float32))
-    oq.quantize_tensor(t, np.float32(448.0 / 5.5), 0)
-    dt = time.perf_counter() - t0
+    ds, (qt, _) = _seconds(lambda: oq.quantize_tensor(t, np.float32(448.0 / 5.5), 0))
+    dt = dq + dg + ds
     flops = 2.0 * rows * rows * K
-    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(blas) if blas else 1),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": (f"MX quantize of A[:{rows}] and B[:{rows}] (8192 columns), fp64 GEMM {rows}x{rows}x{K} "
-                       f"with bf16 rounding, per-tensor cast of {stream_sample} stream elements; "
-                       f"value = sample GEMM FLOPs / oracle time"),
-            "host_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
-            "checksum": float(np.abs(C16).sum())}
+    summary = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+               "seconds": round(dt, 2),
+               "sample": (f"MX quantize of A[:{rows}] and B[:{rows}] ({K} columns), fp64 GEMM {rows}x{rows}x{K}, "
+                          f"per-tensor cast of {stream_sample} stream elements; value = sample GEMM FLOPs / "
+                          f"oracle time (the GEMM on all BLAS threads, the casts on one)"),
+               "parts": {"mx_quantize": {"seconds": round(dq, 2), "threads": 1,
+                                         "gb_s": round(2 * rows * K * (3 + 1 / 32) / dq / 1e9, 3)},
+                         "gemm_ref": {"seconds": round(dg, 2), "threads": _blas_threads(),
+                                      "flops_computed": {"C": flops, "S": flops, "G": flops / 8},
+                                      "tflop_s_C": round(flops / dg / 1e12, 4),
+                                      "tflop_s_C_S_G": round(2.125 * flops / dg / 1e12, 4)},
+                         "stream_cast": {"seconds": round(ds, 2), "threads": 1,
+                                         "gb_s": round(stream_sample * 3 / ds / 1e9, 3)}},
+               **_host_info()}
+    return summary, {"qa": qa, "ea": ea, "qb": qb, "eb": eb, "C": C, "S": S, "C16": C16, "t": t, "qt": qt,
+                     "rows": rows, "stream_sample": stream_sample}
+
+
+def calib_mfma(qa, ea, iters=4000, launches=6):
+    """Matrix-core ceiling on the GEMM's own operands (libfp8calib.so): TFLOP/s and the clock
+    the chip held meanwhile (core cycles over constant-rate ticks)."""
+    import ctypes
+
+    import torch
+
+    from scaled_quantize_gemm_amd.build import CALIB_LIBNAME, LIBDIR
+
+    lib = ctypes.CDLL(os.path.join(LIBDIR, CALIB_LIBNAME))
+    lib.fp8_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp8_calib_mfma_flops.restype = ctypes.c_double
+    lib.fp8_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=qa.device)
+    clocks = torch.zeros((blocks, 2), dtype=torch.int64, device=qa.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        rc = lib.fp8_calib_mfma(qa.data_ptr(), qa.numel(), ea.data_ptr(), ea.numel(), blocks, iters, sink.data_ptr(),
+                                clocks.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"fp8_calib_mfma: {rc}")
+
+    us = _time_us(run, launches, 2)
+    khz = lib.fp8_calib_wall_clock_khz(0)
+    c = clocks.cpu().double()
+    ghz = float((c[:, 0] / c[:, 1]).mean()) * khz / 1e6 if khz > 0 else None
+    return {"tflops": lib.fp8_calib_mfma_flops(blocks, iters) / us / 1e6, "clock_ghz": ghz,
+            "config": f"{blocks} blocks x 8 waves x {iters} x 16 scaled 32x32x64 E4M3 MFMAs on the GEMM's codes"}
 
 
 def _time_us(fn, steps, warmup):
@@ -626,11 +738,151 @@ def k_sweep_rows(sq, workloads, dev, steps, warmup):
     return out
 
 
+def cpu_baseline_workload1():
+    """The oracle's 16-step loop of workload 1 (quantize X_t and W with the delayed scales, fp64
+    GEMM, history and update), the whole loop: us per step."""
+    import numpy as np
+
+    import workloads
+    from oracle import gemm as og, quantize as oq, recipe as orc
+
+    W = workloads.w1_weight().numpy()
+    Xs = [workloads.w1_input(t).numpy() for t in range(16)]
+
+    def loop():
+        st = orc.DelayedState(2, 16)
+        for X in Xs:
+            qx, ax = oq.quantize_tensor(X, st.scale[0], 0)
+            qw, aw = oq.quantize_tensor(W, st.scale[1], 0)
+            og.gemm_ref(qx, 0, st.scale_inv[0], og.TENSOR, qw, 0, st.scale_inv[1], og.TENSOR)
+            st.record(0, ax)
+            st.record(1, aw)
+            st = orc.delayed_update(st, [0, 0])
+
+    dt, _ = _seconds(loop)
+    return {"value": dt * 1e6 / 16, "unit": "us per step", "cores": _blas_threads(), "kind": "oracle",
+            "sample": "the whole 16-step loop at 256x256 (quantizes single-threaded, GEMM on all BLAS threads)",
+            **_host_info()}
+
+
+def cpu_baseline_minigpt(tokens=512):
+    """One step of workload 2 by the oracle on a quarter of the tokens: per layer the three
+    cast-transposes and the fwd / dgrad / wgrad GEMMs; TFLOP/s over the sample's GEMM FLOPs."""
+    import numpy as np
+
+    import workloads
+    from oracle import gemm as og, quantize as oq
+
+    ins = [tuple(t.float().numpy() for t in workloads.w2_layer(li, 0, tokens=tokens))
+           for li in range(len(workloads.MINIGPT_LAYERS))]
+    flops = 0.0
+
+    def step():
+        nonlocal flops
+        flops = 0.0
+        for (x, w, dy) in ins:
+            qx, qxT, _ = oq.cast_transpose(x, np.float32(448 / 5.0), 0)
+            qw, qwT, _ = oq.cast_transpose(w, np.float32(448 / 0.1), 0)
+            qd, qdT, _ = oq.cast_transpose(dy, np.float32(57344 / 5e-3), 1)
+            og.gemm_ref(qx, 0, np.float32(1), og.TENSOR, qw, 0, np.float32(1), og.TENSOR)
+            og.gemm_ref(qd, 1, np.float32(1), og.TENSOR, qwT, 0, np.float32(1), og.TENSOR)
+            og.gemm_ref(qdT, 1, np.float32(1), og.TENSOR, qxT, 0, np.float32(1), og.TENSOR)
+            flops += 3 * 2.0 * x.shape[0] * x.shape[1] * w.shape[0]
+
+    dt, _ = _seconds(step)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"one step of the layer set at {tokens} tokens (a quarter): 9 cast-transposes "
+                      "(single-threaded) and 9 fp64 GEMMs (all BLAS threads)", **_host_info()}
+
+
+def cpu_baseline_blockwise(rows=256):
+    """Workload 3 by the oracle on a row sample: 1x128 quantize of X[:rows], 128x128 quantize of
+    W, fp64 blockwise GEMM rows x 7168 x 7168; TFLOP/s over the sample's GEMM FLOPs."""
+    import workloads
+    from oracle import gemm as og, quantize as oq
+
+    X, W = workloads.w3_inputs()
+    x, w = X[:rows].float().numpy(), W.float().numpy()
+
+    def run():
+        qx, sx = oq.quantize_tile_1x128(x, 0)
+        qw, sw = oq.quantize_block_128x128(w, 0)
+        og.gemm_ref(qx, 0, sx, og.TILE_1x128, qw, 0, sw, og.BLOCK_128x128)
+
+    dt, _ = _seconds(run)
+    flops = 2.0 * rows * w.shape[0] * w.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"X[:{rows}] 1x128 and the whole W 128x128 quantized (single-threaded), fp64 GEMM "
+                      f"{rows}x7168x7168 (all BLAS threads)", **_host_info()}
+
+
+def cpu_baseline_next_rows(rows=256):
+    """Workload 4's fusions by the oracle on a row sample: LayerNorm + per-tensor cast of X[:rows],
+    and the FC1 GEMM of those rows with the SwiGLU epilogue and an E4M3 output."""
+    import numpy as np
+
+    import workloads
+    from oracle import epilogue as oe, gemm as og, layernorm as oln, quantize as oq
+
+    X, W, _ = workloads.w4_inputs()
+    x, w = X[:rows].float().numpy(), W.float().numpy()
+    gamma = np.ones(x.shape[1], np.float32)
+
+    def run():
+        oln.layernorm_quantize(x, gamma, None, 1e-5, 0, 0, scale=np.float32(448 / 5.0))
+        qx = oq.quantize_tensor(x, np.float32(448 / 5.0), 0)[0]
+        qw = oq.quantize_tensor(w, np.float32(448 / 0.1), 0)[0]
+        C, _, _ = og.gemm_ref(qx, 0, np.float32(5 / 448), og.TENSOR, qw, 0, np.float32(0.1 / 448), og.TENSOR)
+        _, y = oe.epilogue_ref(C, None, oe.ACT_SWIGLU)
+        oe.fp8_output(y, np.float32(224.0), 0)
+
+    dt, _ = _seconds(run)
+    flops = 2.0 * rows * w.shape[0] * w.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"LayerNorm + cast of X[:{rows}], quantize of W, fp64 GEMM {rows}x14336x4096, SwiGLU and "
+                      "E4M3 output (elementwise work single-threaded, the GEMM on all BLAS threads)",
+            **_host_info()}
+
+
+def step_parity(sq, ref, C, qa, ea, qb, eb, T, scale):
+    """The timed step's outputs against the oracle on the cpu_baseline sample: MX codes and e8m0
+    bytes of A[:r] and B[:r] and the first stream elements' codes bit for bit; the bf16 GEMM
+    output's top-left r x r block against the stated tolerance |err| <= 2^-18 S + 1 bf16 ulp."""
+    import numpy as np
+    import torch
+
+    from oracle import fp8 as ofp8
+
+    r, n = ref["rows"], ref["stream_sample"]
+    q = torch.empty(n, dtype=torch.uint8, device=T.device)
+    s = np.float32(448.0 / 5.5)
+    sq.fp8_quantize(T[:n], sq.FP8_E4M3, sq.FP8_SCALE_TENSOR, scale=torch.tensor([s], device=T.device), q=q)
+    g = C[:r, :r].float().cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref["C"])
+    bound = 2.0 ** -18 * ref["S"] + ofp8.bf16_ulp(np.maximum(np.abs(ref["C"]), np.abs(g)))
+    pos = ref["S"] > 0
+    return {"sample": f"rows [:{r}] of A and B, C[:{r}, :{r}], stream[:{n}]",
+            "mx_codes_equal": bool(np.array_equal(qa[:r].cpu().numpy(), ref["qa"])
+                                   and np.array_equal(qb[:r].cpu().numpy(), ref["qb"])),
+            "e8m0_equal": bool(np.array_equal(ea[:, :r].cpu().numpy().T, ref["ea"])
+                               and np.array_equal(eb[:, :r].cpu().numpy().T, ref["eb"])),
+            "stream_codes_equal": bool(np.array_equal(q.cpu().numpy(), ref["qt"])),
+            "gemm_frac_within_2^-18_S_plus_1_bf16_ulp": float(np.mean(err <= bound)),
+            "gemm_max_err_over_S": float((err[pos] / ref["S"][pos]).max()),
+            "gemm_equals_bf16_of_oracle": float(np.mean(g == ref["C16"]))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="untimed steps for at least this long before the warmup steps: the chip's clock "
+                         "settles under sustained load (the first steps of a run are ~10%% slower)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device-to-device copy of known size (counter calibration)")
@@ -675,25 +927,22 @@ def main():
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
         return
 
-    if args.workload1:
-        print(json.dumps(workload1_rows(sq, workloads, dev, args.steps, args.warmup)))
-        return
-
-    if args.minigpt:
-        print(json.dumps(minigpt_rows(sq, workloads, dev, args.steps, args.warmup)))
-        return
-
-    if args.blockwise:
-        print(json.dumps(blockwise_rows(sq, workloads, dev, args.steps, args.warmup)))
-        return
+    side_lines = ((args.workload1, workload1_rows, cpu_baseline_workload1),
+                  (args.minigpt, minigpt_rows, cpu_baseline_minigpt),
+                  (args.blockwise, blockwise_rows, cpu_baseline_blockwise),
+                  (args.next_rows, next_rows, cpu_baseline_next_rows))
+    for chosen, rows_fn, base_fn in side_lines:
+        if chosen:
+            out = rows_fn(sq, workloads, dev, args.steps, args.warmup)
+            if not args.no_cpu_baseline:
+                out["cpu_baseline"] = base_fn()
+            print(json.dumps(out))
+            return
 
     if args.k_sweep:
         print(json.dumps(k_sweep_rows(sq, workloads, dev, args.steps, args.warmup)))
         return
 
-    if args.next_rows:
-        print(json.dumps(next_rows(sq, workloads, dev, args.steps, args.warmup)))
-        return
 
     M = N = K = 8192
     NUMEL = 1 << 28
@@ -735,6 +984,13 @@ def main():
         return {names[i]: sum(events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)) / args.steps
                 for i in which}
 
+    # sustained load first, so that the timed steps see the clock the chip holds under it
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     # timed region: events only around the GEMM (every event pair between launches costs the
@@ -795,6 +1051,10 @@ def main():
     cp_gbs = 2 * dY.numel() * 2 / cp_us / 1e3
     del dY, dYs, cq, cqT, cp_dst
 
+    # the matrix cores' ceiling on the GEMM's own operands, and the clock they hold meanwhile
+    ceil = calib_mfma(qa, ea)
+    gemm_counters = _counters("gemm_mx", GEMM_SOURCES)
+
     gemm_flops = 2.0 * M * N * K
     stream_bytes = NUMEL * (2 + 1)  # bf16 read + E4M3 write (amax is a scalar)
     mxq_bytes = M * K * (2 + 1) + M * (K // 32)
@@ -808,9 +1068,12 @@ def main():
         "metric": "FP8 GEMM TFLOP/s (% FP8 MFMA peak) + amax/cast GB/s (% HBM peak)",
         "value": round(value, 2),
         "unit": "TFLOP/s",
+        "value_basis": "GEMM FLOPs of one step / the whole step's time (2^28-element amax + cast, recipe update, "
+                       "MX quantize of A and B, MX GEMM); the GEMM alone is roofline.achieved",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -822,7 +1085,12 @@ def main():
                    "in_dtype": "bf16", "out_dtype": "bf16", "stream_numel": NUMEL},
         "roofline": {"kernel": "gemm_mx", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": _traffic("gemm_mx", GEMM_SOURCES)},
+                     "traffic": _traffic("gemm_mx", GEMM_SOURCES),
+                     "ceiling": round(ceil["tflops"], 1), "frac_of_ceiling": round(gemm_tflops / ceil["tflops"], 4),
+                     "ceiling_clock_ghz": None if ceil["clock_ghz"] is None else round(ceil["clock_ghz"], 3),
+                     "ceiling_config": ceil["config"],
+                     "gemm_clock_ghz": gemm_counters.get("clock_ghz"),
+                     "gemm_mfma_busy": gemm_counters.get("mfma_busy")},
         "roofline_amax_cast": {"kernel": "amax_cast_stream", "bound": "hbm", "achieved": round(stream_gbs, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
                                "traffic": _traffic("amax_cast_stream", QUANT_SOURCES),
@@ -843,7 +1111,10 @@ def main():
         "mx_quantize_gbs": round(mxq_gbs, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        base, ref = cpu_baseline()
+        base["parts"].update(oracle_single_thread_parts())
+        out["cpu_baseline"] = base
+        out["parity"] = step_parity(sq, ref, C, qa, ea, qb, eb, T, scale)
     print(json.dumps(out))
 
 

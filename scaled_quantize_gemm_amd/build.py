@@ -1,6 +1,7 @@
-"""Compile the HIP sources under csrc/ into lib/libscaledfp8.so for gfx950.
+"""Compile the HIP sources under csrc/ into lib/libscaledfp8.so for gfx950, and the
+measurement kernels under calib/ into lib/libfp8calib.so.
 
-Each .hip file is compiled to an object in parallel, then linked into one shared
+Each .hip file is compiled to an object in parallel, then linked into its shared
 library.  Run as ``python -m scaled_quantize_gemm_amd.build`` or call ``build()``.
 """
 
@@ -14,6 +15,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+CALIB = os.path.join(HERE, "calib")
+CALIB_LIBNAME = "libfp8calib.so"
 LIBDIR = os.path.join(HERE, "lib")
 LIBNAME = "libscaledfp8.so"
 ARCH = "gfx950"
@@ -46,27 +49,31 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every csrc/*.hip and link lib/libscaledfp8.so; returns the library path."""
+    """Compile every csrc/*.hip and calib/*.hip and link lib/libscaledfp8.so and
+    lib/libfp8calib.so; returns the FP8 library's path."""
     cc = hipcc()
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    libs = {LIBNAME: [], CALIB_LIBNAME: []}
     jobs_ = []
-    for src in sources:
-        obj = os.path.join(objdir, src[:-4] + ".o")
-        jobs_.append((obj, [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+    for libname, srcdir in ((LIBNAME, CSRC), (CALIB_LIBNAME, CALIB)):
+        for src in sorted(f for f in os.listdir(srcdir) if f.endswith(".hip")):
+            obj = os.path.join(objdir, src[:-4] + ".o")
+            libs[libname].append(obj)
+            jobs_.append((obj, [cc, *HIPCC_FLAGS, "-c", os.path.join(srcdir, src), "-o", obj]))
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(jobs_)))) as ex:
         for (obj, cmd), out in zip(jobs_, ex.map(lambda j: _run(j[1]), jobs_)):
             if verbose and out.strip():
                 print(out)
-    lib = os.path.join(LIBDIR, LIBNAME)
-    tmp = lib + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in jobs_]])
-    os.replace(tmp, lib)
-    if verbose:
-        print(f"built {lib}")
-    return lib
+    for libname, objs in libs.items():
+        lib = os.path.join(LIBDIR, libname)
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
+    return os.path.join(LIBDIR, LIBNAME)
 
 
 if __name__ == "__main__":
