@@ -267,3 +267,17 @@ def test_casts_reject_mis_sized_buffers():
             "scale_inv_out must have")
     _raises(lambda: sq.fp8_recipe_update(_e(16, 3), _e(2), _e(3), [0, 0, 1]), ValueError, "scale must have")
     _raises(lambda: sq.fp8_recipe_update(_e(16, 3), _e(3), _e(3), [0, 0, 1]), ValueError, "GPU tensor")
+
+
+def test_calibration_library_exports_its_header():
+    """include/fp8_calib.h (the measurement kernels bench.py loads) against libfp8calib.so."""
+    from scaled_quantize_gemm_amd.build import CALIB_LIBNAME, LIBDIR
+
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fp8_calib.h")).read(), flags=re.S)
+    names = re.findall(r"^\s*(?:int|double)\s+(fp8_calib_\w+)\s*\(", src, re.M)
+    assert sorted(names) == ["fp8_calib_mfma", "fp8_calib_mfma_flops", "fp8_calib_wall_clock_khz"]
+    lib = ctypes.CDLL(os.path.join(LIBDIR, CALIB_LIBNAME))
+    for name in names:
+        assert hasattr(lib, name), name
+    lib.fp8_calib_mfma_flops.restype = ctypes.c_double
+    assert lib.fp8_calib_mfma_flops(2, 3) == 2 * 8 * 3 * 16 * 2.0 * 32 * 32 * 64
