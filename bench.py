@@ -47,7 +47,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mx_8192_traffic.json")
 # the sources each kernel is built from (a counter summary is current only for these)
-GEMM_SOURCES = ["gemm_pp.h", "gemm_common.h", "gemm_epilogue.h", "common.h"]  # the MX GEMM's kernel and launch
+GEMM_SOURCES = ["gemm_w4.h", "gemm_common.h", "gemm_epilogue.h", "common.h"]  # the MX GEMM's kernel and launch
 QUANT_SOURCES = ["quantize.hip", "quant_rules.h", "common.h"]
 CT_SOURCES = ["cast_transpose.hip", "quant_rules.h", "common.h"]
 

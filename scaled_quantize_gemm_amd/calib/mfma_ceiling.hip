@@ -1,5 +1,5 @@
 // Matrix-core ceiling on given FP8 data, for the GEMM's roofline: every wave issues scaled
-// 32x32x64 FP8 MFMAs back to back (the ping-pong GEMM kernel's instruction, with 8 independent
+// 32x32x64 FP8 MFMAs back to back (the large-tile GEMM kernel's instruction, with 8 independent
 // accumulators per wave), alternating between two operand sets read once from the caller's
 // FP8 codes and e8m0 bytes, so that the data toggles the multipliers as the GEMM's does.  Wave
 // 0 of each block records the core cycle counter and the constant-rate counter around its

@@ -145,4 +145,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// two fp32 -> packed bf16 (a in the low half), round to nearest even, by gfx950's packed
+// conversion instruction: the same finite results as f32_to_bf16_bits, NaN stays NaN (quiet)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 }  // namespace sfp8

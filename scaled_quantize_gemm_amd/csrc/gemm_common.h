@@ -1,4 +1,4 @@
-// Definitions shared by the GEMM kernels (gemm_small.h, gemm_pp.h, gemm_blk.h): operand vector
+// Definitions shared by the GEMM kernels (gemm_small.h, gemm_w4.h, gemm_blk.h): operand vector
 // types, the scaling modes, inline LDS reads with immediate offsets, compile-time unrolling, and
 // the XCD-aware order in which the large-tile kernels walk their tiles.
 #pragma once

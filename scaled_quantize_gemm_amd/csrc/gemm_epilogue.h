@@ -204,15 +204,15 @@ struct Epilogue {
       }
     } else if constexpr (T == EPI_BF16) {
       uint16_t* c = static_cast<uint16_t*>(base) + at;
-      uint32_t b[W];
-#pragma unroll
-      for (int i = 0; i < W; ++i) b[i] = f32_to_bf16_bits(v[i]);
       if (full && W == 4) {
-        const u32x2 w = {b[0] | (b[W > 1 ? 1 : 0] << 16), b[W > 2 ? 2 : 0] | (b[W > 3 ? 3 : 0] << 16)};
+        const u32x2 w = {f32x2_to_bf16x2(v[0], v[W > 1 ? 1 : 0]), f32x2_to_bf16x2(v[W > 2 ? 2 : 0], v[W > 3 ? 3 : 0])};
         __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(c));
       } else if (full && W == 2) {
-        __builtin_nontemporal_store(b[0] | (b[W > 1 ? 1 : 0] << 16), reinterpret_cast<uint32_t*>(c));
+        __builtin_nontemporal_store(f32x2_to_bf16x2(v[0], v[W > 1 ? 1 : 0]), reinterpret_cast<uint32_t*>(c));
       } else {
+        uint32_t b[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i) b[i] = f32_to_bf16_bits(v[i]);
 #pragma unroll
         for (int i = 0; i < W; ++i)
           if (full || i < avail) c[i] = (uint16_t)b[i];

@@ -7,14 +7,15 @@
 // (accumulation-precision bullet); MX gives every 32 numbers a shared scale and DeepSeek-V3
 // scales 1x128 activation runs and 128x128 weight blocks (absmax bullet).
 //
-// Kernels: gemm_small.h (128 x 128 tiles, any shape), gemm_pp.h (256 x 256 ping-pong, per-tensor
-// and MX), gemm_blk.h (256 x 128 / 256 x 64 ping-pong, blockwise and small per-tensor problems).
+// Kernels: gemm_small.h (128 x 128 tiles, any shape), gemm_w4.h (256 x 256, one wave per SIMD,
+// per-tensor and MX), gemm_blk.h (256 x 128 / 256 x 64 ping-pong, blockwise and small per-tensor
+// problems).
 // This file routes a problem to one of them and holds the host-side checks and dispatch.
 #pragma once
 
 #include "gemm_blk.h"
-#include "gemm_pp.h"
 #include "gemm_small.h"
+#include "gemm_w4.h"
 
 namespace sfp8 {
 
@@ -22,7 +23,7 @@ namespace sfp8 {
 // 144- and 192-tile GEMMs of the MiniGPT layer set moved too and its step got 5-7% slower)
 constexpr int64_t kNarrowTiles = 128;
 
-// the kernel for a problem: the 256 x 256 ping-pong kernel (gemm_pp.h) for per-tensor problems
+// the kernel for a problem: the 256 x 256 kernel (gemm_w4.h) for per-tensor problems
 // of at least 256 of its tiles and for MX; the 256 x 128 / 256 x 64 kernel (gemm_blk.h) for the
 // blockwise modes and smaller per-tensor problems; the 128 x 128 kernel (gemm_small.h) where
 // neither applies
@@ -33,7 +34,7 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
     // fewer 256 x 256 tiles than CUs: the 256 x 128 tiles of the blockwise kernel keep twice
     // as many CUs busy (workload 2's per-tensor GEMMs 1.5x faster); from one full wave of
     // tiles on, the 256 x 256 kernel reads less per FLOP and wins
-    const int64_t big_tiles = (int64_t)((M + BIG_BM - 1) / BIG_BM) * ((N + BIG_BN - 1) / BIG_BN);
+    const int64_t big_tiles = (int64_t)((M + W4_BM - 1) / W4_BM) * ((N + W4_BN - 1) / W4_BN);
     if (big_tiles < 256 && 256ll * K < (1ll << 32)) {
       const int64_t tiles = (int64_t)((M + BLK_BM - 1) / BLK_BM) * ((N + BLK_BN - 1) / BLK_BN);
       // still a fraction of the CUs: 256 x 64 tiles double the count
@@ -50,7 +51,7 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
       // offsets; beyond that the 128 x 128 kernel (64-bit addressing) takes the problem
       const int64_t mn = M > N ? M : N;
       const bool offsets32 = 256ll * K < (1ll << 32) && (MODE != MODE_MX || (int64_t)(K / 32) * mn < (1ll << 32));
-      if (offsets32) return launch_pp<MODE, FA, FB, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
+      if (offsets32) return launch_w4<MODE, FA, FB, OUT, FUSED>(A, B, sa, sb, ep, M, N, K, st, what);
     }
   }
   if constexpr (MODE == MODE_BLOCK || MODE == MODE_TILE2) {

@@ -169,9 +169,10 @@ def test_mx_gemm(sq, out, mnk):
     check_gemm(np_of(C), Cr, S, G, K, "mx", out == 1, f"mx {mnk} out{out}")
 
 
-# Shapes with many 256 x 256 tiles on the large-tile kernel: ragged edges, K steps
-# fewer than the pipeline depth and not a multiple of it.
-BIG_CASES = [(2048, 4096, 128), (2148, 4036, 384), (4096, 2304, 1152), (2052, 4100, 256)]
+# Shapes with at least 256 tiles of 256 x 256, so that per-tensor scaling reaches the
+# large-tile kernel too: ragged edges in M and N, and 1, 3, 9 and 2 K stages of 128 (fewer
+# than the stages its loads run ahead, odd counts, a count the unrolled loop does not divide).
+BIG_CASES = [(4096, 4352, 128), (4100, 4036, 384), (4296, 4036, 1152), (4052, 4100, 256)]
 
 
 @pytest.mark.parametrize("mnk", BIG_CASES)

@@ -1,7 +1,7 @@
 """Bit-level GEMM parity on every kernel route.
 
-Three kinds of check, each on every route the dispatcher can take (the 256x256 ping-pong
-kernel with per-tensor and MX scales, the 256x128 and 256x64 kernels with per-tensor,
+Three kinds of check, each on every route the dispatcher can take (the 256x256 kernel with
+one wave per SIMD, per-tensor and MX scales, the 256x128 and 256x64 kernels with per-tensor,
 blockwise and 1x128 x 1x128 scales, the 128x128 fallback with per-tensor and MX scales):
 
 * exact inputs: codes with |value| in [1, 2) (random signs, some zeros) and power-of-two
@@ -77,9 +77,9 @@ def record(label, C_gpu, C_ref, S, out_bf16):
 
 # (name, mode, M, N, K): shapes that reach each kernel (see launch_gemm)
 ROUTES = [
-    ("pp_tensor", "tensor", 4096, 4096, 1024),       # 256 tiles of 256x256: ping-pong kernel
-    ("pp_tensor_longk", "tensor", 4096, 4096, 14336),
-    ("pp_mx", "mx", 1024, 1024, 8192),               # MX: ping-pong kernel at any size
+    ("w4_tensor", "tensor", 4096, 4096, 1024),       # 256 tiles of 256x256: 256x256 kernel
+    ("w4_tensor_longk", "tensor", 4096, 4096, 14336),
+    ("w4_mx", "mx", 1024, 1024, 8192),               # MX: 256x256 kernel at any size
     ("blk128_tensor", "tensor", 2048, 4096, 2048),   # 128 big tiles: 256x128 kernel
     ("blk64_tensor", "tensor", 1024, 2048, 3072),    # 64 tiles of 256x128: 256x64 kernel
     ("blk_block", "block", 1024, 2048, 7168),        # TILE x BLOCK: 256x128 kernel
@@ -192,7 +192,7 @@ def _crafted_operands(n, K, rng):
     return cases, A, B
 
 
-@pytest.mark.parametrize("route", ["pp_tensor", "pp_mx", "blk128_tensor", "blk64_tensor", "blk_block", "blk_tile2",
+@pytest.mark.parametrize("route", ["w4_tensor", "w4_mx", "blk128_tensor", "blk64_tensor", "blk_block", "blk_tile2",
                                    "small_tensor", "small_mx"])
 def test_accumulator_crafted(sq, route):
     """Crafted dot products, one per diagonal output, on every MFMA shape and kernel: the
@@ -202,10 +202,10 @@ def test_accumulator_crafted(sq, route):
     rng = np.random.default_rng(1234)
     n = 256
     cases, A, B = _crafted_operands(n, K, rng)
-    mode = {"pp_tensor": "tensor", "pp_mx": "mx", "blk128_tensor": "tensor", "blk64_tensor": "tensor",
+    mode = {"w4_tensor": "tensor", "w4_mx": "mx", "blk128_tensor": "tensor", "blk64_tensor": "tensor",
             "blk_block": "block", "blk_tile2": "tile2", "small_tensor": "tensor", "small_mx": "mx"}[route]
     # embed the n x n problem where the route needs a larger one; extra rows / columns are zero
-    M, N = {"pp_tensor": (4096, 4096), "blk128_tensor": (2048, 4096), "blk64_tensor": (1024, 2048),
+    M, N = {"w4_tensor": (4096, 4096), "blk128_tensor": (2048, 4096), "blk64_tensor": (1024, 2048),
             "small_tensor": (n, n), "small_mx": (n, n)}.get(route, (n, n))
     Ab = np.zeros((M, K), np.uint8)
     Bb = np.zeros((N, K), np.uint8)
@@ -312,7 +312,7 @@ def test_realistic_matches_model(sq, route, fa):
     record(f"{name} fa={fa} bf16", Cbf, C_ref, S, True)
 
 
-@pytest.mark.parametrize("route", ["pp_tensor", "pp_mx", "blk64_tensor", "blk_block"])
+@pytest.mark.parametrize("route", ["w4_tensor", "w4_mx", "blk64_tensor", "blk_block"])
 def test_adversarial_codes_within_model_bound(sq, route):
     """Uniform random finite codes (40 binades inside a run): >= 99% of outputs equal
     mfma_model bit for bit, the rest lie within its step bound."""

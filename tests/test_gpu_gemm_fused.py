@@ -160,9 +160,10 @@ def test_fused_odd_n(sq, act):
     run_case(sq, "tensor", 33, 517, 256, act, BF16, "f32", True, seed=5)
 
 
-# many tiles of the large-tile kernels (256 x 256 for tensor / MX, 256 x 128 blockwise);
-# ragged M and N, N % 4 == 2 for the unaligned-quad path of the blockwise kernel
-LARGE = {"tensor": (2052, 4100, 256), "mx": (2148, 4036, 384), "block": (2085, 3002, 384), "tile2": (1300, 4100, 256)}
+# many tiles of the large-tile kernels (256 x 256 for tensor (at least 256 tiles) and MX,
+# 256 x 128 blockwise); ragged M and N, N % 4 == 2 for the unaligned-quad paths (tensor and
+# blockwise)
+LARGE = {"tensor": (4100, 4102, 256), "mx": (2148, 4036, 384), "block": (2085, 3002, 384), "tile2": (1300, 4100, 256)}
 LARGE_COMBOS = [(SWIGLU, E4, "bf16", True), (GELU, BF16, "f32", False), (NONE, E5, None, False),
                 (SWIGLU, F32, "f32", False)]
 
