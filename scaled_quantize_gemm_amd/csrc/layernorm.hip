@@ -77,7 +77,7 @@ __device__ __forceinline__ void unpack_chunk(const Chunk<BF16>& c, float (&v)[8]
 // fp32) of neighbouring groups fill their cache lines in one L2.  gamma and beta sit in LDS as
 // fp32 for the block's lifetime; each wave loads its next row while it normalises the current
 // one, so the row's HBM latency overlaps the reductions and the cast.
-template <int FMT, bool BF16, int GRAN, int NCH>
+template <int FMT, bool BF16, int GRAN, int NCH, bool FULL>
 __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, const void* __restrict__ beta, int w_bf16, float eps,
     int64_t rows, int cols, int64_t groups, const float* __restrict__ scale_p, uint32_t* __restrict__ amax_slot,
@@ -85,22 +85,40 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
   extern __shared__ __attribute__((aligned(16))) float ln_smem[];
   float* g_s = ln_smem;         // [cols]
   float* b_s = ln_smem + cols;  // [cols] (zeros without beta)
-  for (int i = threadIdx.x; i < cols; i += 64 * kLnRows) {
-    g_s[i] = w_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(gamma)[i] << 16)
-                    : static_cast<const float*>(gamma)[i];
-    float bv = 0.0f;
-    if (beta != nullptr)
-      bv = w_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(beta)[i] << 16)
-                  : static_cast<const float*>(beta)[i];
-    b_s[i] = bv;
-  }
-  __syncthreads();
+  // gamma and beta to LDS as fp32, 8 columns per thread and pass (cols is a multiple of 8;
+  // both are 16-byte aligned); each wave issues its first row's loads before the fill, so
+  // that their latency overlaps it
+  auto fill = [&](const void* src, float* dst) {
+    for (int i = 8 * threadIdx.x; i < cols; i += 8 * 64 * kLnRows) {
+      float w[8];
+      if (src == nullptr) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = 0.0f;
+      } else if (w_bf16) {
+        const u32x4 h = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + i);
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          w[2 * k] = bf16_lo(hw[k]);
+          w[2 * k + 1] = bf16_hi(hw[k]);
+        }
+      } else {
+        const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+        const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i + 4);
+        w[0] = f0.x; w[1] = f0.y; w[2] = f0.z; w[3] = f0.w;
+        w[4] = f1.x; w[5] = f1.y; w[6] = f1.z; w[7] = f1.w;
+      }
+      *reinterpret_cast<float4*>(dst + i) = make_float4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<float4*>(dst + i + 4) = make_float4(w[4], w[5], w[6], w[7]);
+    }
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row addresses in SGPRs
   const int nbx = gridDim.x >> 3, xcd = blockIdx.x & 7;
   const int64_t g_end = groups * (xcd + 1) / 8;
-  const int nch = cols >> 3;
+  // FULL: cols == 512 NCH, every lane holds NCH whole chunks (no per-chunk tests)
+  const int nch = FULL ? 64 * NCH : cols >> 3;
   float s = 1.0f;
   if constexpr (GRAN == FP8_SCALE_TENSOR) s = *scale_p;
   // this lane's scale column: run (lane + 64p) / 16 of 1x128 tiles, (lane + 64p) / 4 of MX
@@ -121,6 +139,9 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
         if (lane + 64 * p < nch) load_chunk<BF16>(x, row * cols + 8 * (lane + 64 * p), raw[p]);
     }
   }
+  fill(gamma, g_s);
+  fill(beta, b_s);
+  __syncthreads();
   for (; grp < g_end; grp += nbx) {
     const bool live = row < rows;
     float v[NCH][8];
@@ -264,15 +285,20 @@ static void launch_ln(int nch_blocks, const void* x, const void* gamma, const vo
       n = 256;
     return n;
   }();
-#define SFP8_LN(N)                                                                                                   \
+#define SFP8_LN_F(N, F)                                                                                              \
   do {                                                                                                               \
     int per_cu = 0;                                                                                                  \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_quant_kernel<FMT, BF16, GRAN, N>, 64 * kLnRows,     \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_quant_kernel<FMT, BF16, GRAN, N, F>, 64 * kLnRows,  \
                                                      lds) != hipSuccess || per_cu < 1)                              \
       per_cu = 1;                                                                                                    \
     const int64_t per_xcd = std::min<int64_t>((int64_t)per_cu * (cus / 8), (groups + 7) / 8);                        \
-    hipLaunchKernelGGL((ln_quant_kernel<FMT, BF16, GRAN, N>), dim3((unsigned)(8 * per_xcd)), dim3(64 * kLnRows), lds, \
-                       st, x, gamma, beta, w_bf16, eps, rows, cols, groups, scale, slot, q, sinv, mu, rs);          \
+    hipLaunchKernelGGL((ln_quant_kernel<FMT, BF16, GRAN, N, F>), dim3((unsigned)(8 * per_xcd)), dim3(64 * kLnRows),  \
+                       lds, st, x, gamma, beta, w_bf16, eps, rows, cols, groups, scale, slot, q, sinv, mu, rs);      \
+  } while (0)
+#define SFP8_LN(N)                          \
+  do {                                      \
+    if (cols == 512 * (N)) SFP8_LN_F(N, true); \
+    else SFP8_LN_F(N, false);               \
   } while (0)
   switch (nch_blocks) {
     case 1: SFP8_LN(1); break;
@@ -282,6 +308,7 @@ static void launch_ln(int nch_blocks, const void* x, const void* gamma, const vo
     default: SFP8_LN(16); break;
   }
 #undef SFP8_LN
+#undef SFP8_LN_F
 }
 
 template <int FMT, bool BF16>
