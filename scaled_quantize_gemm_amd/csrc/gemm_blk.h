@@ -31,17 +31,10 @@ namespace sfp8 {
 // 4 columns per row (4r + j) leave as one 8-byte (bf16) or 16-byte (fp32) store.
 
 constexpr int BLK_BM = 256, BLK_BN = 128, BLK_BK = 128;
-constexpr int BLK_B_OFF = BLK_BM * BLK_BK;               // 32 KB of A
-constexpr int BLK_SA_OFF = BLK_B_OFF + BLK_BN * BLK_BK;  // 16 KB of B
-constexpr int BLK_SB_OFF = BLK_SA_OFF + 1024;            // 256 row scales
-constexpr int BLK_STAGE = BLK_SB_OFF + 1024;             // 4 copies x 64 of the block scale
 constexpr int BLK_NST = 3;
 
-// the tile row held at LDS row q of a 64-row slab layout (tile i's MFMA row t at 16i + t is
-// slab row 4t + i)
-__device__ __forceinline__ int blk_row_of(int q) { return (q & ~63) + 4 * (q & 15) + ((q >> 4) & 3); }
-// the B row (output column) held at LDS row q of a slab of 16 NT columns: MFMA tile j's
-// column t at LDS row 16j + t is slab column NT t + j (NT = 4: the same map as the rows)
+// the tile row (A) or output column (B) held at LDS row q of a slab of 16 nt rows or columns:
+// MFMA tile j's row / column t at LDS row 16j + t is slab row / column nt t + j
 __device__ __forceinline__ int blk_col_of(int q, int nt) {
   return (q & ~(16 * nt - 1)) + nt * (q & 15) + ((q >> 4) & (nt - 1));
 }
@@ -52,25 +45,30 @@ __device__ __forceinline__ int blk_pos(int q, int c) { return c ^ (((q >> 1) ^ (
 // per 1x128 run along K: one per column per stage, [K/128][N]) or MODE_TENSOR (no scale loads;
 // the MFMAs accumulate straight into acc and the epilogue multiplies by sa * sb: the 256 x 128
 // tile gives small per-tensor problems twice the tiles of the 256 x 256 kernel)
-// the tile-width-dependent shape of the kernel below: NT MFMA column tiles per wave slab of SW
-// columns; the B rows of a stage are BN x 128 B, loaded as NB of the stage's NOPS 1 KB
-// operations (OPW per wave).
-template <int BN>
+// the tile-shape-dependent layout of the kernel below: TI MFMA row tiles and NT column tiles per
+// wave slab of SH x SW; the A rows of a stage are BM x 128 B and the B rows BN x 128 B, loaded as
+// NA + NB = NOPS 1 KB operations (OPW per wave).  BM = 128 (per-tensor only) halves the slab
+// height: twice the tiles again for problems that leave most CUs idle.
+template <int BM, int BN>
 struct BlkShape {
-  static constexpr int NT = BN / 32, SW = BN / 2, NB = BN / 8, NOPS = 32 + NB, OPW = NOPS / 8;
-  static constexpr int SA_OFF = BLK_B_OFF + BN * BLK_BK, SB_OFF = SA_OFF + 1024, STAGE = SB_OFF + 1024;
+  static constexpr int TI = BM / 64, SH = BM / 4, NT = BN / 32, SW = BN / 2;
+  static constexpr int NA = BM / 8, NB = BN / 8, NOPS = NA + NB, OPW = NOPS / 8;
+  static constexpr int B_OFF = BM * BLK_BK, SA_OFF = B_OFF + BN * BLK_BK, SB_OFF = SA_OFF + 1024,
+                       STAGE = SB_OFF + 1024;
 };
 
-template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN>
+template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN, int BM>
 __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                           const float* __restrict__ sa_p,
                                                           const float* __restrict__ sb_p, const EpiParams ep, int M,
                                                           int N, int K, int tiles_m, int tiles_n) {
   constexpr bool TENSOR = MODE == MODE_TENSOR;
   static_assert(BN == BLK_BN || (BN == 64 && TENSOR), "256 x 64 tiles serve per-tensor scaling only");
-  using Shape = BlkShape<BN>;
-  constexpr int NT = Shape::NT, SW = Shape::SW, NOPS = Shape::NOPS, OPW = Shape::OPW;
-  constexpr int SA_OFF = Shape::SA_OFF, SB_OFF = Shape::SB_OFF, STAGE = Shape::STAGE;
+  static_assert(BM == BLK_BM || (BM == 128 && TENSOR), "128-row tiles serve per-tensor scaling only");
+  using Shape = BlkShape<BM, BN>;
+  constexpr int TI = Shape::TI, SH = Shape::SH, NT = Shape::NT, SW = Shape::SW, NA = Shape::NA;
+  constexpr int NOPS = Shape::NOPS, OPW = Shape::OPW;
+  constexpr int B_OFF = Shape::B_OFF, SA_OFF = Shape::SA_OFF, SB_OFF = Shape::SB_OFF, STAGE = Shape::STAGE;
   constexpr int NST = BLK_NST, D = NST - 1, U = NST;
   static_assert(NOPS % 8 == 0, "every wave issues the same number of loads");
   static_assert(NST * STAGE <= 160 * 1024, "LDS ring must fit the 160 KB of a CU");
@@ -82,10 +80,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   const int g = lane >> 4, r = lane & 15;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BLK_BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int nk = K / BLK_BK;
 
-  // ---- loads: NOPS x 1 KB of tile data per stage, OPW per wave (ops 0..31 are A, then B), and
+  // ---- loads: NOPS x 1 KB of tile data per stage, OPW per wave (ops 0..NA-1 are A, then B), and
   //      one scale load per wave (waves 0-3: 64 row scales each; 4-7: a copy of the block scale)
   const int lim_a = M - m0, lim_b = N - n0;
   const uint64_t a_bytes = (uint64_t)lim_a * K, b_bytes = (uint64_t)lim_b * K;
@@ -101,9 +99,9 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   uint32_t od[6];
 #pragma unroll
   for (int i = 0; i < OPW; ++i) {
-    const int o = wave * OPW + i, local = o < 32 ? o : o - 32;
+    const int o = wave * OPW + i, local = o < NA ? o : o - NA;
     const int slot = local * 64 + lane, q = slot >> 3, c = blk_pos(q, slot & 7);
-    const int row = o < 32 ? blk_row_of(q) : blk_col_of(q, NT), lim = o < 32 ? lim_a : lim_b;
+    const int row = o < NA ? blk_col_of(q, TI) : blk_col_of(q, NT), lim = o < NA ? lim_a : lim_b;
     od[i] = (uint32_t)(row < lim ? row : lim - 1) * (uint32_t)K + c * 16;
   }
   const int nkb = nk;
@@ -136,7 +134,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     uint8_t* buf = smem + st * STAGE;
 #pragma unroll
     for (int i = 0; i < OPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave * OPW + i < 32 ? ra : rb, (lds_ptr_t)(buf + (wave * OPW + i) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave * OPW + i < NA ? ra : rb, (lds_ptr_t)(buf + (wave * OPW + i) * 1024),
                                                16, od[i], ks * BLK_BK, 0, 0);
     if constexpr (!TENSOR)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(buf + s_lds), 4, s_voff, ks * s_step, 0, 0);
@@ -150,7 +148,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 
   // ---- per-lane LDS bases per stage (immediates add the tile offsets)
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const int slab_a = grp * 128 + wr * 64, slab_b = wc * SW;
+  const int slab_a = grp * (2 * SH) + wr * SH, slab_b = wc * SW;
   uint32_t a_lo[NST], a_hi[NST], b_lo[NST], b_hi[NST], s_a[NST], s_b[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
@@ -158,18 +156,18 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     const int qa = slab_a + r, qb = slab_b + r;  // tile 0's rows; tile i adds 16 rows = 2048 B
     a_lo[st] = base + qa * 128 + (blk_pos(qa, g) << 4);
     a_hi[st] = base + qa * 128 + (blk_pos(qa, g + 4) << 4);
-    b_lo[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g) << 4);
-    b_hi[st] = base + BLK_B_OFF + qb * 128 + (blk_pos(qb, g + 4) << 4);
+    b_lo[st] = base + B_OFF + qb * 128 + (blk_pos(qb, g) << 4);
+    b_hi[st] = base + B_OFF + qb * 128 + (blk_pos(qb, g + 4) << 4);
     s_a[st] = base + SA_OFF + (slab_a + 16 * g) * 4;
     s_b[st] = base + SB_OFF + (MODE == MODE_TILE2 ? (slab_b + 4 * r) * 4 : 0);
   }
 
-  v4f acc[4][Shape::NT];
+  v4f acc[Shape::TI][Shape::NT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  v8i fa[4], fb[Shape::NT];
+  v8i fa[Shape::TI], fb[Shape::NT];
   float fsa[16], fsb[4] = {0.f, 0.f, 0.f, 0.f};
   // the fold's scale factors for this K step: sa[row] * sb (block) in sc[0..15], or
   // sa[row] * sb[column j] in sc[16 j + e] for two 1x128 operands
@@ -183,8 +181,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     // same lane address + 16 rows of 128 B
     fa[0] = pack(ds_read16<0 * 2048>(a_lo[ST]), ds_read16<0 * 2048>(a_hi[ST]));
     fa[1] = pack(ds_read16<1 * 2048>(a_lo[ST]), ds_read16<1 * 2048>(a_hi[ST]));
-    fa[2] = pack(ds_read16<2 * 2048>(a_lo[ST]), ds_read16<2 * 2048>(a_hi[ST]));
-    fa[3] = pack(ds_read16<3 * 2048>(a_lo[ST]), ds_read16<3 * 2048>(a_hi[ST]));
+    if constexpr (TI == 4) {
+      fa[TI > 2 ? 2 : 0] = pack(ds_read16<2 * 2048>(a_lo[ST]), ds_read16<2 * 2048>(a_hi[ST]));
+      fa[TI > 3 ? 3 : 0] = pack(ds_read16<3 * 2048>(a_lo[ST]), ds_read16<3 * 2048>(a_hi[ST]));
+    }
     fb[0] = pack(ds_read16<0 * 2048>(b_lo[ST]), ds_read16<0 * 2048>(b_hi[ST]));
     fb[1] = pack(ds_read16<1 * 2048>(b_lo[ST]), ds_read16<1 * 2048>(b_hi[ST]));
     if constexpr (NT == 4) {
@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   auto compute = [&]() {
     if constexpr (TENSOR) {
 #pragma unroll
-      for (int t = 0; t < 4 * NT; ++t) {
+      for (int t = 0; t < TI * NT; ++t) {
         acc[t / NT][t % NT] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t / NT], fb[t % NT],
                                                                                 acc[t / NT][t % NT], FA, FB, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -309,7 +309,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       }, std::make_integer_sequence<int, U>{});
   }
 
-  // ---- epilogue: acc[i][j][jj] is tile row slab + 16g + 4jj + i, column slab + NT r + j
+  // ---- epilogue: acc[i][j][jj] is tile row slab + TI (4g + jj) + i, column slab + NT r + j
   Epilogue<OUT, FUSED> epi(ep);
   float scale = 1.0f;
   if constexpr (TENSOR) scale = sa_p[0] * sb_p[0];
@@ -322,8 +322,8 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gm = m0 + slab_a + 16 * g + 4 * jj + i;
+      for (int i = 0; i < TI; ++i) {
+        const int gm = m0 + slab_a + TI * (4 * g + jj) + i;
         if (gm >= M) continue;
         float v[Shape::NT];
 #pragma unroll
@@ -342,12 +342,12 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
 
 // per-tensor problems with fewer 256 x 128 tiles than this run on 256 x 64 tiles (at 200, the
 
-// launch over BLK_BM x BN tiles of C; the caller has checked the 32-bit offsets
-template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN>
+// launch over BM x BN tiles of C; the caller has checked the 32-bit offsets
+template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN, int BM = BLK_BM>
 static int launch_blk(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, const EpiParams& ep, int M,
                       int N, int K, hipStream_t st, const char* what) {
-  const int tiles_m = (M + BLK_BM - 1) / BLK_BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, BN>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, BN, BM>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
                      static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m, tiles_n);
   return check_launch(what);
 }

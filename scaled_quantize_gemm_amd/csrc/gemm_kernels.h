@@ -22,6 +22,8 @@ namespace sfp8 {
 // per-tensor problems with fewer 256 x 128 tiles than this run on 256 x 64 tiles (at 200, the
 // 144- and 192-tile GEMMs of the MiniGPT layer set moved too and its step got 5-7% slower)
 constexpr int64_t kNarrowTiles = 128;
+// ... and those whose 128 x 64 tiles number at most this run on them (one tile per CU)
+constexpr int64_t kSmallTileMax = 256;
 
 // the kernel for a problem: the 256 x 256 kernel (gemm_w4.h) for per-tensor problems
 // of at least 256 of its tiles and for MX; the 256 x 128 / 256 x 64 kernel (gemm_blk.h) for the
@@ -37,8 +39,14 @@ static int launch_gemm(const uint8_t* A, const uint8_t* B, const void* sa, const
     const int64_t big_tiles = (int64_t)((M + W4_BM - 1) / W4_BM) * ((N + W4_BN - 1) / W4_BN);
     if (big_tiles < 256 && 256ll * K < (1ll << 32)) {
       const int64_t tiles = (int64_t)((M + BLK_BM - 1) / BLK_BM) * ((N + BLK_BN - 1) / BLK_BN);
-      // still a fraction of the CUs: 256 x 64 tiles double the count
-      if (tiles < kNarrowTiles) return launch_blk<MODE, FA, FB, OUT, FUSED, 64>(A, B, sa, sb, ep, M, N, K, st, what);
+      // still a fraction of the CUs: 256 x 64 tiles double the count, and 128 x 64 tiles
+      // double it again where that still fits one tile per CU
+      if (tiles < kNarrowTiles) {
+        const int64_t small = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
+        if (small <= kSmallTileMax)
+          return launch_blk<MODE, FA, FB, OUT, FUSED, 64, 128>(A, B, sa, sb, ep, M, N, K, st, what);
+        return launch_blk<MODE, FA, FB, OUT, FUSED, 64>(A, B, sa, sb, ep, M, N, K, st, what);
+      }
       return launch_blk<MODE, FA, FB, OUT, FUSED, BLK_BN>(A, B, sa, sb, ep, M, N, K, st, what);
     }
   }

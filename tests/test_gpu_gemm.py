@@ -113,7 +113,8 @@ def test_tensor_scaled_gemm(sq, fa, fb, out, mnk):
 
 
 # per-tensor problems below 128 tiles of 256 x 128 run on 256 x 64 tiles, from 128 tiles on on
-# 256 x 128 tiles (and from 256 tiles of 256 x 256 on the 256 x 256 kernel): both sides of each
+# 256 x 128 tiles, 128 x 64 tiles where at most 256 of them cover C (and from 256 tiles of
+# 256 x 256 on the 256 x 256 kernel): both sides of each
 # boundary, with ragged last tiles, against the oracle on sampled rows
 @pytest.mark.parametrize("mnk", [
     (256, 127 * 128, 256),       # 127 tiles of 256 x 128: 256 x 64 tiles
@@ -122,6 +123,10 @@ def test_tensor_scaled_gemm(sq, fa, fb, out, mnk):
     (2 * 256, 64 * 128, 128),    # 2 x 64 = 128: 256 x 128 tiles
     (3840, 4096, 128),           # 15 x 16 = 240 tiles of 256 x 256: 256 x 128 tiles
     (4096, 4096 - 3, 128),       # 256 tiles of 256 x 256, ragged N: the 256 x 256 kernel
+    (1024, 2048, 256),           # 64 tiles of 256 x 128 and 256 of 128 x 64: 128 x 64 tiles
+    (1024, 2049, 256),           # 264 of 128 x 64: 256 x 64 tiles
+    (1000, 1500, 384),           # 192 of 128 x 64, ragged M and N: 128 x 64 tiles
+    (100, 700, 128),             # one tile row shorter than 128: 128 x 64 tiles
 ])
 def test_tensor_gemm_tile_width_boundaries(sq, mnk):
     M, N, K = mnk

@@ -1,7 +1,7 @@
 """Bit-level GEMM parity on every kernel route.
 
 Three kinds of check, each on every route the dispatcher can take (the 256x256 kernel with
-one wave per SIMD, per-tensor and MX scales, the 256x128 and 256x64 kernels with per-tensor,
+one wave per SIMD, per-tensor and MX scales, the 256x128, 256x64 and 128x64 kernels with per-tensor,
 blockwise and 1x128 x 1x128 scales, the 128x128 fallback with per-tensor and MX scales):
 
 * exact inputs: codes with |value| in [1, 2) (random signs, some zeros) and power-of-two
@@ -81,7 +81,8 @@ ROUTES = [
     ("w4_tensor_longk", "tensor", 4096, 4096, 14336),
     ("w4_mx", "mx", 1024, 1024, 8192),               # MX: 256x256 kernel at any size
     ("blk128_tensor", "tensor", 2048, 4096, 2048),   # 128 big tiles: 256x128 kernel
-    ("blk64_tensor", "tensor", 1024, 2048, 3072),    # 64 tiles of 256x128: 256x64 kernel
+    ("blk64_tensor", "tensor", 1536, 2048, 3072),    # 96 tiles of 256x128, 384 of 128x64: 256x64 kernel
+    ("blk128x64_tensor", "tensor", 1024, 2048, 3072),  # 256 tiles of 128x64: 128x64 kernel
     ("blk_block", "block", 1024, 2048, 7168),        # TILE x BLOCK: 256x128 kernel
     ("blk_tile2", "tile2", 1024, 1152, 4096),        # TILE x TILE: 256x128 kernel
     ("small_tensor", "tensor", 2, 1000, 1024),       # M < 4: 128x128 kernel
@@ -192,8 +193,8 @@ def _crafted_operands(n, K, rng):
     return cases, A, B
 
 
-@pytest.mark.parametrize("route", ["w4_tensor", "w4_mx", "blk128_tensor", "blk64_tensor", "blk_block", "blk_tile2",
-                                   "small_tensor", "small_mx"])
+@pytest.mark.parametrize("route", ["w4_tensor", "w4_mx", "blk128_tensor", "blk64_tensor", "blk128x64_tensor",
+                                   "blk_block", "blk_tile2", "small_tensor", "small_mx"])
 def test_accumulator_crafted(sq, route):
     """Crafted dot products, one per diagonal output, on every MFMA shape and kernel: the
     hand-derived values of the accumulation rules, and mfma_model bit for bit."""
@@ -203,9 +204,10 @@ def test_accumulator_crafted(sq, route):
     n = 256
     cases, A, B = _crafted_operands(n, K, rng)
     mode = {"w4_tensor": "tensor", "w4_mx": "mx", "blk128_tensor": "tensor", "blk64_tensor": "tensor",
-            "blk_block": "block", "blk_tile2": "tile2", "small_tensor": "tensor", "small_mx": "mx"}[route]
+            "blk128x64_tensor": "tensor", "blk_block": "block", "blk_tile2": "tile2", "small_tensor": "tensor", "small_mx": "mx"}[route]
     # embed the n x n problem where the route needs a larger one; extra rows / columns are zero
-    M, N = {"w4_tensor": (4096, 4096), "blk128_tensor": (2048, 4096), "blk64_tensor": (1024, 2048),
+    M, N = {"w4_tensor": (4096, 4096), "blk128_tensor": (2048, 4096), "blk64_tensor": (1536, 2048),
+            "blk128x64_tensor": (1024, 2048),
             "small_tensor": (n, n), "small_mx": (n, n)}.get(route, (n, n))
     Ab = np.zeros((M, K), np.uint8)
     Bb = np.zeros((N, K), np.uint8)
@@ -312,7 +314,7 @@ def test_realistic_matches_model(sq, route, fa):
     record(f"{name} fa={fa} bf16", Cbf, C_ref, S, True)
 
 
-@pytest.mark.parametrize("route", ["w4_tensor", "w4_mx", "blk64_tensor", "blk_block"])
+@pytest.mark.parametrize("route", ["w4_tensor", "w4_mx", "blk64_tensor", "blk128x64_tensor", "blk_block"])
 def test_adversarial_codes_within_model_bound(sq, route):
     """Uniform random finite codes (40 binades inside a run): >= 99% of outputs equal
     mfma_model bit for bit, the rest lie within its step bound."""
