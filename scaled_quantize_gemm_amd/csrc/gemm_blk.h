@@ -57,13 +57,25 @@ struct BlkShape {
                        STAGE = SB_OFF + 1024;
 };
 
+// Block b of a launch over the tiles of a tiles_m x tiles_n tiling in tile_of's order: on XCD
+// b % 8, that XCD's tiles from index idx0 on, `sub` blocks per tile (part = which 1/sub of the
+// tile's columns the block takes).  False where the XCD has no such tile.
+__device__ __forceinline__ bool tile_part_of(int b, int tiles_m, int tiles_n, int idx0, int sub, int& tm, int& tn,
+                                             int& part) {
+  const int T = tiles_m * tiles_n, xcd = b & 7, j = b >> 3, idx = idx0 + j / sub;
+  part = j - (j / sub) * sub;
+  if (idx >= (T >> 3) + (xcd < (T & 7) ? 1 : 0)) return false;
+  tile_of(8 * idx + xcd, tiles_m, tiles_n, tm, tn);
+  return true;
+}
+
 template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN, int BM>
 __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                           const float* __restrict__ sa_p,
                                                           const float* __restrict__ sb_p, const EpiParams ep, int M,
-                                                          int N, int K, int tiles_m, int tiles_n) {
+                                                          int N, int K, int tiles_m, int tiles_n, int idx0, int sub) {
   constexpr bool TENSOR = MODE == MODE_TENSOR;
-  static_assert(BN == BLK_BN || (BN == 64 && TENSOR), "256 x 64 tiles serve per-tensor scaling only");
+  static_assert(BN == BLK_BN || BN == 64, "256 x 128 or 256 x 64 tiles");
   static_assert(BM == BLK_BM || (BM == 128 && TENSOR), "128-row tiles serve per-tensor scaling only");
   using Shape = BlkShape<BM, BN>;
   constexpr int TI = Shape::TI, SH = Shape::SH, NT = Shape::NT, SW = Shape::SW, NA = Shape::NA;
@@ -78,9 +90,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, wi = wave & 3, wr = wi >> 1, wc = wi & 1;
   const int g = lane >> 4, r = lane & 15;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  int tm, tn, part;
+  if (!tile_part_of(blockIdx.x, tiles_m, tiles_n, idx0, sub, tm, tn, part)) return;
+  const int m0 = tm * BM, n0 = (tn * sub + part) * BN;
+  if (n0 >= N) return;  // the second half of a last tile column at most 64 wide
   const int nk = K / BLK_BK;
 
   // ---- loads: NOPS x 1 KB of tile data per stage, OPW per wave (ops 0..NA-1 are A, then B), and
@@ -116,8 +129,10 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     const int row = wave * 64 + lane;
     s_voff = (uint32_t)(row < lim_a ? row : lim_a - 1) * 4;
   } else if constexpr (MODE == MODE_BLOCK) {
-    const uint64_t bytes = ((uint64_t)tiles_n * nkb - (uint64_t)tn * nkb) * 4;
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb_p + (size_t)tn * nkb), (short)0,
+    // the tile lies in weight-block column n0 / 128 (its [K/128] scales are contiguous)
+    const int bc = n0 >> 7, nbc = (N + 127) >> 7;
+    const uint64_t bytes = (uint64_t)(nbc - bc) * nkb * 4;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sb_p + (size_t)bc * nkb), (short)0,
                                            (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull), kBufferFlags);
     s_voff = 0;
   } else {
@@ -159,7 +174,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     b_lo[st] = base + B_OFF + qb * 128 + (blk_pos(qb, g) << 4);
     b_hi[st] = base + B_OFF + qb * 128 + (blk_pos(qb, g + 4) << 4);
     s_a[st] = base + SA_OFF + (slab_a + 16 * g) * 4;
-    s_b[st] = base + SB_OFF + (MODE == MODE_TILE2 ? (slab_b + 4 * r) * 4 : 0);
+    s_b[st] = base + SB_OFF + (MODE == MODE_TILE2 ? (slab_b + NT * r) * 4 : 0);
   }
 
   v4f acc[Shape::TI][Shape::NT];
@@ -205,16 +220,17 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
     if constexpr (MODE == MODE_BLOCK) {
       fsb[0] = __uint_as_float(ds_read4<0>(s_b[ST]));
     } else {
-      const u32x4 sbv = ds_read16<0>(s_b[ST]);  // columns 4r .. 4r+3 of the slab
+      // columns NT r .. NT r + NT - 1 of the slab (NT = 2: the first two of the four read)
+      const u32x4 sbv = ds_read16<0>(s_b[ST]);
       fsb[0] = __uint_as_float(sbv.x);
       fsb[1] = __uint_as_float(sbv.y);
       fsb[2] = __uint_as_float(sbv.z);
       fsb[3] = __uint_as_float(sbv.w);
     }
   };
-  // 16 MFMAs, each partial folded into its accumulators four MFMAs later (at 4096 x 7168 x
-  // 7168, folding one MFMA later was 25% slower and two MFMAs later 1.5%):
-  // acc[i][j][jj] += p * (sa[row 16g + 4jj + i] * sb[block] or sb[column 4r + j])
+  // TI x NT MFMAs (16, or 8 on 64-wide tiles), each partial folded into its accumulators four
+  // MFMAs later (at 4096 x 7168 x 7168, folding one MFMA later was 25% slower and two MFMAs
+  // later 1.5%): acc[i][j][jj] += p * (sa[row 16g + 4jj + i] * sb[block] or sb[column NT r + j])
   auto compute = [&]() {
     if constexpr (TENSOR) {
 #pragma unroll
@@ -226,22 +242,22 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       return;
     } else {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kFoldLag = 4;
-    v4f p[16];
+    constexpr int kFoldLag = 4, NM = TI * NT;
+    v4f p[NM];
     auto fold = [&](int t) {
-      const int i = t >> 2, j = t & 3;
+      const int i = t / NT, j = t % NT;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         acc[i][j][jj] = fmaf(p[t][jj], sc[(MODE == MODE_BLOCK ? 0 : 16 * j) + 4 * jj + i], acc[i][j][jj]);
     };
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      p[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t >> 2], fb[t & 3], zero, FA, FB, 0, 0, 0, 0);
+    for (int t = 0; t < NM; ++t) {
+      p[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[t / NT], fb[t % NT], zero, FA, FB, 0, 0, 0, 0);
       if (t >= kFoldLag) fold(t - kFoldLag);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int t = 16 - kFoldLag; t < 16; ++t) fold(t);
+    for (int t = NM - kFoldLag; t < NM; ++t) fold(t);
     }
   };
   // the scale products, formed while the other wave group runs its MFMAs, so that the fold
@@ -252,7 +268,7 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
       for (int e = 0; e < 16; ++e) sc[e] = fsa[e] * fsb[0];
     } else if constexpr (MODE == MODE_TILE2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[16 * j + e] = fsa[e] * fsb[j];
     }
@@ -340,15 +356,37 @@ __global__ void __launch_bounds__(512, 1) gemm_blk_kernel(const uint8_t* __restr
   epi.finish(lane, reinterpret_cast<uint32_t*>(smem));
 }
 
-// per-tensor problems with fewer 256 x 128 tiles than this run on 256 x 64 tiles (at 200, the
-
-// launch over BM x BN tiles of C; the caller has checked the 32-bit offsets
+// launch over BM x BN tiles of C; the caller has checked the 32-bit offsets.
+// A 256 x 128 tiling whose last round of tiles would leave at least three quarters of an XCD's
+// 32 CUs idle (tile_of gives each XCD a contiguous run of tiles, which its CUs take 32 at a
+// time, one block per CU) runs as two launches: the whole rounds, then what is left of each
+// XCD's run as twice as many 256 x 64 tiles, which take less than a whole tile's time each
+// (workload 3's wgrad, 7168 x 7168 x 4096 with 4 tiles per XCD left: 256 -> 243 us).  With
+// half the CUs left busy the halves gained nothing (its forward, 16 tiles per XCD left:
+// 215 -> 220 us), so that case keeps the 256 x 128 tiles.
 template <int MODE, int FA, int FB, int OUT, bool FUSED, int BN, int BM = BLK_BM>
 static int launch_blk(const uint8_t* A, const uint8_t* B, const void* sa, const void* sb, const EpiParams& ep, int M,
                       int N, int K, hipStream_t st, const char* what) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const float* fa = static_cast<const float*>(sa);
+  const float* fb = static_cast<const float*>(sb);
+  if constexpr (BN == BLK_BN && BM == BLK_BM) {
+    constexpr int kXcdCus = 32;
+    const int T = tiles_m * tiles_n, per = T >> 3;
+    const int whole = per / kXcdCus * kXcdCus;                // tile indices every XCD runs in whole rounds
+    const int left = per - whole + ((T & 7) != 0 ? 1 : 0);  // at most this many tiles per XCD after them
+    if (whole > 0 && left > 0 && 4 * left <= kXcdCus) {
+      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, BN, BM>), dim3(8 * whole), dim3(512), 0, st, A, B,
+                         fa, fb, ep, M, N, K, tiles_m, tiles_n, 0, 1);
+      const int rc = check_launch(what);
+      if (rc != FP8_OK) return rc;
+      hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, 64, BM>), dim3(8 * 2 * left), dim3(512), 0, st, A,
+                         B, fa, fb, ep, M, N, K, tiles_m, tiles_n, whole, 2);
+      return check_launch(what);
+    }
+  }
   hipLaunchKernelGGL((gemm_blk_kernel<MODE, FA, FB, OUT, FUSED, BN, BM>), dim3(tiles_m * tiles_n), dim3(512), 0, st, A, B,
-                     static_cast<const float*>(sa), static_cast<const float*>(sb), ep, M, N, K, tiles_m, tiles_n);
+                     fa, fb, ep, M, N, K, tiles_m, tiles_n, 0, 1);
   return check_launch(what);
 }
 

@@ -85,6 +85,12 @@ ROUTES = [
     ("blk128x64_tensor", "tensor", 1024, 2048, 3072),  # 256 tiles of 128x64: 128x64 kernel
     ("blk_block", "block", 1024, 2048, 7168),        # TILE x BLOCK: 256x128 kernel
     ("blk_tile2", "tile2", 1024, 1152, 4096),        # TILE x TILE: 256x128 kernel
+    # 272 tiles of 256x128 (34 per XCD): 32 per XCD on 256x128 tiles, the other 2 as 256x64
+    # halves in a second launch, among them tiles of the last tile row and of the last tile
+    # column (128, 40 and 76 columns wide: the second half full, absent, 12 wide)
+    ("blk_tensor_split", "tensor", 2048, 4352, 1024),
+    ("blk_block_split", "block", 2048, 4264, 1024),
+    ("blk_tile2_split", "tile2", 2000, 4300, 1024),
     ("small_tensor", "tensor", 2, 1000, 1024),       # M < 4: 128x128 kernel
     ("small_mx", "mx", 6, 512, 2048),                # MX, M not a multiple of 4: 128x128 kernel
 ]
