@@ -157,32 +157,49 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
   __shared__ uint32_t lds[128 * kBwPitch];
   __shared__ uint32_t cred[8][128];
   __shared__ float cscale[128];
-  const int64_t nkb = cols >> 7, nrb = rows >> 7;
+  const int64_t nkb = cols >> 7, nrb = rows >> 7, ntiles = nkb * nrb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r16 = t >> 4, cg = t & 15;
+  uint32_t amax_acc = 0;  // per tensor: this thread's |x| bits max over its tiles
   // tile order.  Blockwise modes: row-band major (a band's blocks read whole source rows).
   // Per tensor: bands of 8 tile rows walked column by column, so that the blocks in flight
   // together write 1 KB runs of each qT row instead of 128-byte pieces spread over all of
   // them (workload 4's dY 8192 x 14336: 99 -> 91 us, the rate of a device-to-device copy with
   // the same read:write mix; 64-row bands helped dY more and X, W less)
-  int64_t rb, kb;
-  if constexpr (KIND == kBwTensor) {
-    constexpr int64_t SR = 8;
-    const int64_t band = blockIdx.x / (SR * nkb), first = band * SR;
-    const int64_t h = nrb - first < SR ? nrb - first : SR;
-    const int64_t in = blockIdx.x - band * SR * nkb;
-    rb = first + in % h;
-    kb = in / h;
-  } else {
-    rb = blockIdx.x / nkb;
-    kb = blockIdx.x - rb * nkb;
-  }
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int r16 = t >> 4, cg = t & 15;
-  const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
+  auto tile_rc = [&](int64_t ix, int64_t& rb, int64_t& kb) {
+    if constexpr (KIND == kBwTensor) {
+      constexpr int64_t SR = 8;
+      const int64_t band = ix / (SR * nkb), first = band * SR;
+      const int64_t h = nrb - first < SR ? nrb - first : SR;
+      const int64_t in = ix - band * SR * nkb;
+      rb = first + in % h;
+      kb = in / h;
+    } else {
+      rb = ix / nkb;
+      kb = ix - rb * nkb;
+    }
+  };
   // the tile stays as loaded (packed bf16: 16 VGPRs) until the cast widens it: widened at the
   // load, the 1x128 mode held 110 VGPRs (2 blocks per CU) and the others ~70 (3); now 56-60 (4)
   Raw8<BF16> raw[4];
+  auto load_tile = [&](int64_t ix) {
+    int64_t rb, kb;
+    tile_rc(ix, rb, kb);
+    const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) raw[p] = load_raw8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols);
+    for (int p = 0; p < 4; ++p) raw[p] = load_raw8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols);
+  };
+  // tile ix = blockIdx.x, + gridDim.x, ... (the blockwise launches have one block per tile; the
+  // per-tensor launch is capped at the blocks resident at once, see launch_ct); each tile's
+  // loads are issued before the previous tile's transpose
+  auto tile = [&](int64_t ix) {
+  int64_t rb, kb;
+  tile_rc(ix, rb, kb);
+  const int64_t base = rb * 128 * cols + kb * 128 + cg * 8;
+  if constexpr (KIND != kBwTensor) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) raw[p] = load_raw8<BF16>(x, base + (int64_t)(r16 + 32 * p) * cols);
+  }
   uint32_t m[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) m[p] = raw_amax_bits<BF16>(raw[p]);
@@ -193,20 +210,8 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
     for (int p = 0; p < 4; ++p) srow[p] = sc;
 #pragma unroll
     for (int e = 0; e < 8; ++e) scol[e] = sc;
-    if (amax_slot != nullptr) {
-      uint32_t mx = m[0];
 #pragma unroll
-      for (int p = 1; p < 4; ++p) mx = mx > m[p] ? mx : m[p];
-      mx = wave_max_u32(mx);
-      if (lane == 0) cred[wave][0] = mx;
-      __syncthreads();
-      if (t == 0) {
-        uint32_t bm = cred[0][0];
-#pragma unroll
-        for (int w = 1; w < 8; ++w) bm = bm > cred[w][0] ? bm : cred[w][0];
-        if (bm > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_slot, bm);
-      }
-    }
+    for (int p = 0; p < 4; ++p) amax_acc = amax_acc > m[p] ? amax_acc : m[p];
   } else if constexpr (TILE) {
     // row runs: the 16 lanes sharing r16
 #pragma unroll
@@ -291,6 +296,9 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
     lds[(r16 + 32 * p) * kBwPitch + cg * 2] = c0;
     lds[(r16 + 32 * p) * kBwPitch + cg * 2 + 1] = c1;
   }
+  // the next tile's loads (per tensor: the blockwise launches run one tile per block)
+  if constexpr (KIND == kBwTensor)
+    if (ix + gridDim.x < ntiles) load_tile(ix + gridDim.x);  // this tile's codes are out of raw
   __syncthreads();
   // transpose: 4 source rows x 4 source columns per dword quad
   const int rg = t & 31, cgt = t >> 5;
@@ -315,22 +323,56 @@ __global__ void __launch_bounds__(512) cast_transpose_bw_kernel(const void* __re
       __builtin_nontemporal_store(o[j],
                                   reinterpret_cast<uint32_t*>(qT + (kb * 128 + 4 * cq + j) * rows + rb * 128 + 4 * rg));
   }
+  };
+  if constexpr (KIND == kBwTensor) {
+    load_tile(blockIdx.x);
+    for (int64_t ix = blockIdx.x; ix < ntiles; ix += gridDim.x) {
+      if (ix != (int64_t)blockIdx.x) __syncthreads();  // the previous tile's transpose is done with lds
+      tile(ix);
+    }
+  } else {
+    tile(blockIdx.x);
+  }
+  // per tensor: the block's amax into the slot with one atomic.  One atomic per 128 x 128 tile
+  // (a block per tile) cost workload 4's dY 16 us of 87 when the slot starts each call at zero,
+  // as it does in a training step: while atomics queue at the slot, the plain reads that should
+  // filter them return stale values.
+  if constexpr (KIND == kBwTensor) {
+    if (amax_slot != nullptr) {
+      const uint32_t mx = wave_max_u32(amax_acc);
+      __syncthreads();
+      if (lane == 0) cred[wave][0] = mx;
+      __syncthreads();
+      if (t == 0) {
+        uint32_t bm = cred[0][0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) bm = bm > cred[w][0] ? bm : cred[w][0];
+        if (bm > __hip_atomic_load(amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_slot, bm);
+      }
+    }
+  }
 }
 
 template <int FMT, bool BF16>
 static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* scale, float* amax_slot, uint8_t* q,
                      uint8_t* qT, hipStream_t st) {
   const int64_t ntiles = ((rows + kCtTile - 1) / kCtTile) * ((cols + kCtTile - 1) / kCtTile);
-  // one block per tile: capping the grid (a persistent loop over tiles) measured 1-5% slower
-  // at workload 4's shapes (8192 x 4096, 14336 x 4096, 8192 x 14336 bf16)
-  const int64_t blocks = ntiles < 0x7FFFFFFF ? ntiles : 0x7FFFFFFF;
+  // 64 x 64 tiles: the grid is capped at 8 blocks per CU (those resident at once), which loop
+  // over the tiles, so that the amax takes one atomic per block, not per tile (see the per-tensor
+  // launch below; in the slot's first use of a step atomics queue and the reads that filter them
+  // go stale)
+  const int64_t cap = 8ll * device_cus();
+  const int64_t blocks = ntiles < cap ? ntiles : cap;
   if (rows % 128 == 0 && cols % 128 == 0 && (rows >> 7) * (cols >> 7) < 0x7FFFFFFF) {
     // 128 x 128 tiles, the blockwise kernel with the per-tensor scale: whole 128-byte lines of q
     // and qT (8192 x 14336 bf16: 88-91 us against 132 us on 64 x 64 tiles, inputs and outputs
     // beyond the last-level cache)
     // 20 KB of unused dynamic LDS hold residency at 3 blocks per CU (41 KB each of 160 KB): at
-    // the 4 its registers allow, this launch measured 2-5% slower at workload 4's shapes
-    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwTensor>), dim3((unsigned)((rows >> 7) * (cols >> 7))),
+    // the 4 its registers allow, this launch measured 2-5% slower at workload 4's shapes.
+    // The grid is those resident blocks (fp32 input: 2 per CU, its registers allow no more),
+    // each looping over tiles, so that one atomic per block (not per tile) carries the amax
+    const int64_t t128 = (rows >> 7) * (cols >> 7), cap = (BF16 ? 3ll : 2ll) * device_cus();
+    hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwTensor>), dim3((unsigned)(t128 < cap ? t128 : cap)),
                        dim3(512), kCtTensorLdsPad, st, x, rows, cols, q, nullptr, qT, nullptr, scale,
                        reinterpret_cast<uint32_t*>(amax_slot));
     return check_launch("fp8_cast_transpose");

@@ -27,29 +27,36 @@ __device__ __forceinline__ uint8_t cast_one(float x, float s) {
   return (uint8_t)w;
 }
 
-// Block-wide unsigned max (256 threads) -> returned to every thread.
-__device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* red) {
+// Block-wide unsigned max (NW waves) -> returned to every thread.
+template <int NW>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < 4; ++i) r = r > red[i] ? r : red[i];
+  for (int i = 1; i < NW; ++i) r = r > red[i] ? r : red[i];
   return r;
 }
 
 // ------------------------------------------------------------------ per-tensor (delayed)
 //
-// Flat stream over n elements in pieces of 8 (16 bytes of bf16).  A block takes 2 x 256
+// Flat stream over n elements in pieces of 8 (16 bytes of bf16).  A block takes 2 x 1024
 // pieces per pass of a grid-stride loop; the pieces of one load instruction are consecutive
 // across the wave's lanes, so every instruction reads 1 KB (bf16) contiguous.  amax is
 // reduced per block and max-ed into *amax_slot with one unsigned atomic per block (|x| bits
 // of non-negative floats order like the floats; NaN wins).
+// The grid is capped at 4 blocks of 1024 threads per CU (two rounds of the resident ones).  The
+// atomics decide it: in a training step the slot starts each call at zero, and with a block
+// per 4096 elements (32768 blocks of 256 threads on 2^28) the 2^28-element cast took 156 us
+// instead of the 126 it takes when the slot already holds the maximum (the plain reads that
+// filter the atomics return stale values while atomics queue at the slot); 1024 blocks of
+// 1024 threads take 131 / 128 us.
 
-constexpr int kTensorThreads = 256;
+constexpr int kTensorThreads = 1024;
 constexpr int kTensorPieces = 2;
-constexpr int64_t kTensorMaxBlocks = 32768;
+constexpr int kTensorBlocksPerCu = 4;
 
 // Cast diagnostics (DIAG): per element, saturated = |fp32(x s)| > fmax (so the code was
 // clipped), underflowed = x finite and non-zero but its code is +-0, nan = x is NaN; block
@@ -73,8 +80,9 @@ __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void
                                                                       uint32_t* __restrict__ amax_slot,
                                                                       uint8_t* __restrict__ q,
                                                                       unsigned long long* __restrict__ counts) {
-  __shared__ uint32_t red[4];
-  __shared__ uint32_t cred[DIAG ? 3 : 1][4];
+  constexpr int NW = kTensorThreads / 64;
+  __shared__ uint32_t red[NW];
+  __shared__ uint32_t cred[DIAG ? 3 : 1][NW];
   uint32_t cnt[3] = {0, 0, 0};
   const float s = *scale_p;
   const int64_t npieces = n >> 3;
@@ -127,10 +135,12 @@ __global__ void __launch_bounds__(kTensorThreads) quant_tensor_kernel(const void
       if ((threadIdx.x & 63) == 0) cred[k][threadIdx.x >> 6] = v;
     }
   }
-  uint32_t r = block_max_u32_256(mxf, red);  // (its barrier also publishes cred)
+  uint32_t r = block_max_u32<NW>(mxf, red);  // (its barrier also publishes cred)
   if constexpr (DIAG) {
     if (threadIdx.x < 3) {
-      const uint32_t tot = cred[threadIdx.x][0] + cred[threadIdx.x][1] + cred[threadIdx.x][2] + cred[threadIdx.x][3];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += cred[threadIdx.x][w];
       if (tot != 0) atomicAdd(counts + threadIdx.x, (unsigned long long)tot);
     }
   }
@@ -344,7 +354,7 @@ static int launch_quant(const void* x, int64_t rows, int64_t cols, int gran, con
     const int64_t per_block = (int64_t)kTensorThreads * kTensorPieces * 8;
     int64_t blocks = (n + per_block - 1) / per_block;
     if (blocks < 1) blocks = 1;
-    if (blocks > kTensorMaxBlocks) blocks = kTensorMaxBlocks;
+    if (blocks > (int64_t)kTensorBlocksPerCu * device_cus()) blocks = (int64_t)kTensorBlocksPerCu * device_cus();
     hipLaunchKernelGGL((quant_tensor_kernel<FMT, BF16, false>), dim3((unsigned)blocks), dim3(kTensorThreads), 0, st,
                        x, n, scale, reinterpret_cast<uint32_t*>(amax_slot), q, nullptr);
   } else if (gran == FP8_SCALE_TILE_1x128) {
@@ -420,7 +430,7 @@ extern "C" int fp8_quantize_diag(const void* x, int x_dtype, int64_t rows, int64
   const int64_t per_block = (int64_t)kTensorThreads * kTensorPieces * 8;
   int64_t blocks = (n + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
-  if (blocks > kTensorMaxBlocks) blocks = kTensorMaxBlocks;
+  if (blocks > (int64_t)kTensorBlocksPerCu * device_cus()) blocks = (int64_t)kTensorBlocksPerCu * device_cus();
   const dim3 grid((unsigned)blocks), block(kTensorThreads);
   uint32_t* slot = reinterpret_cast<uint32_t*>(amax_slot);
   const bool bf = x_dtype == HP_BF16;
