@@ -121,8 +121,7 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
   const int nch = FULL ? 64 * NCH : cols >> 3;
   float s = 1.0f;
   if constexpr (GRAN == FP8_SCALE_TENSOR) s = *scale_p;
-  // this lane's scale column: run (lane + 64p) / 16 of 1x128 tiles, (lane + 64p) / 4 of MX
-  float* const sinv_tile = static_cast<float*>(sinv) + (int64_t)(lane >> 4) * rows;
+  // this lane's scale column: run (lane + 64p) / 4 of MX
   uint8_t* const sinv_mx = static_cast<uint8_t*>(sinv) + (int64_t)(lane >> 2) * rows;
   uint32_t lane_amax = 0u;
 
@@ -196,11 +195,8 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
       // rewrite) is a per-row, wave-uniform branch, and finite rows take the float max with an
       // abs modifier and no rewrite.
       const bool nan_row = __builtin_amdgcn_readfirstlane(__builtin_isfinite(mean) && __builtin_isfinite(rs) ? 0 : 1);
-#pragma unroll
-      for (int p = 0; p < NCH; ++p) {
-        const int c = lane + 64 * p;
-        // whole 4- and 16-lane groups share the branch: nch is a multiple of 4 (MX) / 16 (1x128)
-        if (c >= nch) continue;
+      // y = fma((x - mean) rs, gamma, beta) of chunk c from the centred values xc, rs given
+      auto normalise = [&](const float (&xc)[8], int c, float rs, float (&y)[8]) {
         const float4 g0 = *reinterpret_cast<const float4*>(g_s + 8 * c);
         const float4 g1 = *reinterpret_cast<const float4*>(g_s + 8 * c + 4);
         const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
@@ -209,20 +205,39 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
           const float4 b1 = *reinterpret_cast<const float4*>(b_s + 8 * c + 4);
           const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[p][i] = fmaf(v[p][i] * rs, g[i], bb[i]);
+          for (int i = 0; i < 8; ++i) y[i] = fmaf(xc[i] * rs, g[i], bb[i]);
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] * rs * g[i];
+          for (int i = 0; i < 8; ++i) y[i] = xc[i] * rs * g[i];
+        }
+      };
+      // 1x128: each chunk's group max and this lane's own max, kept for the cast after the scales
+      uint32_t run_max[GRAN == FP8_SCALE_TILE_1x128 ? NCH : 1], own_max[GRAN == FP8_SCALE_TILE_1x128 ? NCH : 1];
+#pragma unroll
+      for (int p = 0; p < NCH; ++p) {
+        const int c = lane + 64 * p;
+        // whole 4- and 16-lane groups share the branch: nch is a multiple of 4 (MX) / 16 (1x128)
+        if (c >= nch) {
+          if constexpr (GRAN == FP8_SCALE_TILE_1x128) run_max[p] = own_max[p] = 0u;
+          continue;
+        }
+        // 1x128 keeps the centred values for a second normalisation after the row's scales
+        // (holding all of y instead took 216 VGPRs, 2 waves per SIMD)
+        float y[8];
+        normalise(v[p], c, rs, y);
+        if constexpr (GRAN != FP8_SCALE_TILE_1x128) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[p][i] = y[i];
         }
         uint32_t m;
         if (nan_row) {
           m = 0u;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) m = m > abs_bits(v[p][i]) ? m : abs_bits(v[p][i]);
+          for (int i = 0; i < 8; ++i) m = m > abs_bits(y[i]) ? m : abs_bits(y[i]);
         } else {
           float mf = 0.0f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[p][i]));
+          for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(y[i]));
           m = __float_as_uint(mf);
         }
         const uint32_t own = m;  // this lane's |y| bits max (NaN bits only on NaN rows)
@@ -230,10 +245,9 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
         if constexpr (GRAN == FP8_SCALE_TENSOR) {
           lane_amax = lane_amax > m ? lane_amax : m;
         } else if constexpr (GRAN == FP8_SCALE_TILE_1x128) {
-          m = group_max_u32<16>(m);
-          float sc_inv;
-          current_scale<FMT>(m, sc, sc_inv);
-          if ((lane & 15) == 0) sinv_tile[(int64_t)(4 * p) * rows + row] = sc_inv;
+          run_max[p] = group_max_u32<16>(m);
+          own_max[p] = own;
+          continue;  // cast below, once the row's scales are known
         } else {
           m = group_max_u32<4>(m);
           uint32_t code;
@@ -243,6 +257,37 @@ __global__ void __launch_bounds__(64 * kLnRows) ln_quant_kernel(
         u32x2 codes = cast8<FMT>(v[p], sc, 0u);
         if (nan_row) codes = cast8<FMT>(v[p], sc, own);
         __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + base + 8 * c));
+      }
+      if constexpr (GRAN == FP8_SCALE_TILE_1x128) {
+        // the row's cols/128 (<= 64) run scales at once, lane L taking run L, instead of every
+        // 16-lane group dividing for its own run in each chunk (two correctly rounded divisions
+        // per 4 runs: 4.5 us of 28 on 8192 x 4096).  Run L's max is chunk L/4's in group L%4;
+        // its scale goes back to the 16 lanes of that group.
+        uint32_t a = 0u;
+#pragma unroll
+        for (int p = 0; p < NCH; ++p) {
+          const uint32_t t = (uint32_t)__shfl((int)run_max[p], 16 * (lane & 3), 64);
+          a = (lane >> 2) == p ? t : a;
+        }
+        float run_sc, run_sinv;
+        current_scale<FMT>(a, run_sc, run_sinv);
+        // the second normalisation must not be merged with the first (that would keep every y
+        // live across the scale step): rs and the chunk index pass through empty asm
+        float rs2 = rs;
+        int lane2 = lane;
+        asm volatile("" : "+v"(rs2), "+v"(lane2));
+        if (lane < (nch >> 4)) static_cast<float*>(sinv)[(int64_t)lane * rows + row] = run_sinv;  // [cols/128][rows]
+#pragma unroll
+        for (int p = 0; p < NCH; ++p) {
+          const int c = lane + 64 * p;
+          const float sc = __shfl(run_sc, (lane >> 4) + 4 * p, 64);
+          if (c >= nch) continue;
+          float y[8];
+          normalise(v[p], lane2 + 64 * p, rs2, y);
+          u32x2 codes = cast8<FMT>(y, sc, 0u);
+          if (nan_row) codes = cast8<FMT>(y, sc, own_max[p]);
+          __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(q + base + 8 * c));
+        }
       }
     }
     row = row_n;
