@@ -18,9 +18,12 @@ def sq():
 
 
 # 128-aligned shapes take the 128 x 128 kernel, the others the 64 x 64 kernel; (1408, 384) and
-# (1152, 640) have 11 and 9 tile rows, so the 128 x 128 kernel's last band of 8 tile rows is partial
+# (1152, 640) have 11 and 9 tile rows, so the 128 x 128 kernel's last band of 8 tile rows is partial.
+# Both launches cap their grids at the blocks resident at once (3 per CU for the 128 x 128
+# kernel's per-tensor mode, 8 for the 64 x 64 one), the blocks looping over tiles: (4096, 3200)
+# has 800 tiles of 128 x 128 and (3000, 2900) 2162 of 64 x 64, so some blocks take two tiles
 SHAPES = [(1, 1), (64, 64), (128, 192), (100, 37), (3, 1000), (200, 136), (257, 130), (2048, 768), (64, 2304),
-          (128, 128), (256, 384), (384, 128), (1408, 384), (1152, 640)]
+          (128, 128), (256, 384), (384, 128), (1408, 384), (1152, 640), (4096, 3200), (3000, 2900)]
 
 
 @pytest.mark.parametrize("fmt", [ofp8.E4M3, ofp8.E5M2])
