@@ -120,7 +120,7 @@ def _decode(q, fmt, gran, scale):
 
 def emulate_gemm(A, fmt_a, sa, gran_a, B, fmt_b, sb, gran_b, rows=None, cols=None, out_bf16=False,
                  chunk=1 << 24):
-    """C = A . B^T as the matrix cores and this build's kernels compute it.
+    """C = A . B^T as the matrix cores and this library's kernels compute it.
 
     Scales follow the oracle's conventions: per tensor a float32 scalar, TILE_1x128
     [K/128][rows], BLOCK_128x128 [ceil(rows/128)][K/128], MX e8m0 codes [rows][K/32].

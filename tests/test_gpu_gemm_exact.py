@@ -18,7 +18,7 @@ blockwise and 1x128 x 1x128 scales, the 128x128 fallback with per-tensor and MX 
   output must lie within its step bound.
 * the stated tolerance: the fraction of outputs within |err| <= 2^-18 S (+ 1 bf16 ulp) of
   the oracle and max err / S are computed for every case and kept in
-  ``gpurun_out/gemm_tolerance.json`` (printed too).
+  ``gemm_tolerance.json`` in the run's output folder (printed too).
 """
 
 import json
