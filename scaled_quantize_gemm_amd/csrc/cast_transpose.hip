@@ -15,6 +15,8 @@
 //            (4 consecutive source rows) to each of 4 rows of qT; 16 lanes cover 64
 //            contiguous bytes of a qT row.
 // Tiles that are partial or whose rows are not 16-byte aligned take an element-wise path.
+#include <algorithm>
+
 #include "quant_rules.h"
 
 namespace sfp8 {
@@ -369,9 +371,15 @@ static int launch_ct(const void* x, int64_t rows, int64_t cols, const float* sca
     // beyond the last-level cache)
     // 20 KB of unused dynamic LDS hold residency at 3 blocks per CU (41 KB each of 160 KB): at
     // the 4 its registers allow, this launch measured 2-5% slower at workload 4's shapes.
-    // The grid is those resident blocks (fp32 input: 2 per CU, its registers allow no more),
-    // each looping over tiles, so that one atomic per block (not per tile) carries the amax
-    const int64_t t128 = (rows >> 7) * (cols >> 7), cap = (BF16 ? 3ll : 2ll) * device_cus();
+    // The grid is capped so that the blocks loop over tiles and fewer atomics carry the amax:
+    // up to 16 tiles per CU, at the resident blocks (fp32 input: 2 per CU, its registers allow
+    // no more); above, at 6/7 of the tiles and at most 24 blocks per CU, so that the first
+    // blocks take two tiles.  Slot cleared / kept, bf16, us: workload 4's X (2048 tiles) 28-31 /
+    // 27 (one block per tile: 42 / 26), W (3584) 46 / 45 (56 / 42; 4096 blocks or more: 54 / 43),
+    // dY (7168) 90 / 88 (105 / 87; resident blocks only: 96 / 96; 4096-6144 blocks: 90-92 /
+    // 89-90)
+    const int64_t t128 = (rows >> 7) * (cols >> 7), cus = device_cus();
+    const int64_t cap = t128 <= 16 * cus ? (BF16 ? 3 : 2) * cus : std::min<int64_t>(24 * cus, t128 * 6 / 7);
     hipLaunchKernelGGL((cast_transpose_bw_kernel<FMT, BF16, kBwTensor>), dim3((unsigned)(t128 < cap ? t128 : cap)),
                        dim3(512), kCtTensorLdsPad, st, x, rows, cols, q, nullptr, qT, nullptr, scale,
                        reinterpret_cast<uint32_t*>(amax_slot));
