@@ -48,9 +48,22 @@ __global__ void __launch_bounds__(256) recipe_update_kernel(float* __restrict__ 
   float* h = hist + col;
   const uint32_t first = __float_as_uint(h[0]);
   uint32_t m = first;
-  for (int i = 1; i < H; ++i) {
-    uint32_t v = __float_as_uint(h[(size_t)i * n]);
-    m = v > m ? v : m;
+  // 16 rows at a time: their 17 loads (the 17th for the shift) in flight together, then the
+  // shifted stores (row i <- row i + 1); the rows of a chunk are stored only after all its loads,
+  // and a later chunk loads rows no earlier chunk stores.  One row per round trip measured
+  // 4.7 us per call at H = 16.
+  for (int i0 = 0; i0 < H; i0 += 16) {
+    float v[17];
+#pragma unroll
+    for (int k = 0; k < 17; ++k) v[k] = i0 + k < H ? h[(size_t)(i0 + k) * n] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t b = __float_as_uint(v[k]);
+      if (i0 + k < H) m = b > m ? b : m;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (i0 + k + 1 < H) h[(size_t)(i0 + k) * n] = v[k + 1];
   }
   if (m > 0u && m < 0x7F800000u) {
     float r = fm / __uint_as_float(m);
@@ -59,7 +72,6 @@ __global__ void __launch_bounds__(256) recipe_update_kernel(float* __restrict__ 
     scale[col] = s;
     scale_inv[col] = 1.0f / s;
   }
-  for (int i = 0; i + 1 < H; ++i) h[(size_t)i * n] = h[(size_t)(i + 1) * n];
   h[(size_t)(H - 1) * n] = __uint_as_float(first);
   h[0] = 0.0f;
 }
