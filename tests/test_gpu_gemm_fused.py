@@ -179,6 +179,22 @@ def test_fused_large(sq, mode, combo):
     run_case(sq, mode, M, N, K, act, out, bias_kind, with_aux, seed=M + 3 * act + out, rows=r)
 
 
+# blockwise problems whose 256 x 128 tiles leave at most 8 per XCD after the whole rounds (306
+# and 272 tiles): the rest run as 256 x 64 halves in a second launch, fused epilogues included
+LARGE_SPLIT = {"block": (2085, 4264, 256), "tile2": (2000, 4300, 256)}
+
+
+@pytest.mark.parametrize("combo", LARGE_COMBOS[:3])
+@pytest.mark.parametrize("mode", ["block", "tile2"])
+def test_fused_split_launch(sq, mode, combo):
+    M, N, K = LARGE_SPLIT[mode]
+    act, out, bias_kind, with_aux = combo
+    rng = np.random.default_rng(M + N + 1)
+    r = np.sort(rng.choice(M, 160, replace=False))
+    r[-1] = M - 1
+    run_case(sq, mode, M, N, K, act, out, bias_kind, with_aux, seed=M + 5 * act + out, rows=r)
+
+
 @pytest.mark.parametrize("mode", ["tensor", "mx", "block"])
 def test_fused_plain_equals_fp8_gemm(sq, mode):
     """act NONE, no bias: the same fp32 values as fp8_gemm, bit for bit, and the FP8 output's
