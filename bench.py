@@ -1032,7 +1032,8 @@ def main():
     per.update(averages(events, tuple(range(GEMM))))
 
     # the standalone amax + cast of the 2^28-element tensor, back to back on its own: its HBM
-    # roofline (inside the step it also absorbs the write-back of the GEMM's output)
+    # roofline (its amax slot holds the maximum after the first launch, so no block's atomic
+    # fires; inside the step each call starts on the slot the recipe update has just cleared)
     standalone = 20
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
